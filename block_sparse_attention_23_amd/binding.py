@@ -1,0 +1,166 @@
+"""Thin ctypes binding of libsol.so (the C ABI in include/sol.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  torch supplies device memory and the stream.  There
+is no fallback: a missing library or a non-GPU tensor raises.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+from . import build as _build
+
+SOL_BF16, SOL_F32 = 0, 1
+
+_FUNCS = {
+    "sol_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
+    "sol_pool": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 5
+                 + [ctypes.c_void_p] * 4),
+    "sol_attn_fwd": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4
+                     + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "sol_attn_fwd_dbg": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4
+                         + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                            ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                            ctypes.c_void_p, ctypes.c_void_p]),
+    "sol_attn_dense": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4
+                       + [ctypes.c_void_p, ctypes.c_void_p]),
+    "sol_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+}
+
+_LIB = None
+
+
+class SolError(RuntimeError):
+    def __init__(self, func, status):
+        self.status = status
+        super().__init__(f"{func} failed: {status_string(status)} (status {status})")
+
+
+def library_path():
+    return _build.LIB
+
+
+def lib():
+    """The loaded libsol.so; raises if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(_build.LIB):
+            raise RuntimeError(
+                f"{_build.LIB} is missing: build it with "
+                "`python -m block_sparse_attention_23_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(_build.LIB)
+        for name, (res, args) in _FUNCS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def status_string(status):
+    return lib().sol_status_string(int(status)).decode()
+
+
+def _check(func, status):
+    if status != 0:
+        raise SolError(func, status)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return SOL_BF16
+    if t.dtype == torch.float32:
+        return SOL_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _tokens(*ts):
+    q = ts[0]
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU (no CPU path exists)")
+        if t.dim() != 3 or not t.is_contiguous():
+            raise ValueError("token tensors must be contiguous [H][L][d]")
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must share shape, dtype and device")
+    return q.shape
+
+
+def _stream_ptr(stream, device):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def nblocks(L, B):
+    return (L + B - 1) // B
+
+
+def workspace_bytes(H, L, d, B):
+    return int(lib().sol_workspace_bytes(H, L, d, B))
+
+
+def alloc_workspace(H, L, d, B, device):
+    n = workspace_bytes(H, L, d, B)
+    if n == 0:
+        raise ValueError(f"unsupported shape H={H} L={L} d={d} B={B}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def pool(q, k, v, B, stream=None):
+    """Block means of q and k and block sums of v, fp32 [H][N][d]."""
+    H, L, d = _tokens(q, k, v)
+    N = nblocks(L, B)
+    outs = [torch.empty((H, N, d), dtype=torch.float32, device=q.device) for _ in range(3)]
+    with torch.cuda.device(q.device):
+        _check("sol_pool", lib().sol_pool(q.data_ptr(), k.data_ptr(), v.data_ptr(), H, L, d, B,
+                                          _dtype_code(q), outs[0].data_ptr(), outs[1].data_ptr(),
+                                          outs[2].data_ptr(), _stream_ptr(stream, q.device)))
+    return tuple(outs)
+
+
+def attn_fwd(q, k, v, B, beta, out=None, kept=None, workspace=None, stream=None, debug=False):
+    """Sol-Attn forward.  Returns (out, kept_counts) or, with debug=True,
+    (out, kept_counts, sel_mask [H][N][ceil(N/32)] int32 bits, tau [H][N])."""
+    H, L, d = _tokens(q, k, v)
+    N = nblocks(L, B)
+    if out is None:
+        out = torch.empty_like(q)
+    if kept is None:
+        kept = torch.empty((H, N), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(H, L, d, B, q.device)
+    args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), H, L, d, B, float(beta), _dtype_code(q),
+            out.data_ptr(), kept.data_ptr(), workspace.data_ptr(), workspace.numel(),
+            _stream_ptr(stream, q.device)]
+    with torch.cuda.device(q.device):
+        if not debug:
+            _check("sol_attn_fwd", lib().sol_attn_fwd(*args))
+            return out, kept
+        W = (N + 31) // 32
+        mask = torch.zeros((H, N, W), dtype=torch.int32, device=q.device)
+        tau = torch.empty((H, N), dtype=torch.float32, device=q.device)
+        _check("sol_attn_fwd_dbg", lib().sol_attn_fwd_dbg(*args, mask.data_ptr(), tau.data_ptr()))
+        return out, kept, mask, tau
+
+
+def attn_dense(q, k, v, out=None, stream=None):
+    """Dense softmax(q k^T / sqrt(d)) v on the same tile machinery."""
+    H, L, d = _tokens(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    with torch.cuda.device(q.device):
+        _check("sol_attn_dense", lib().sol_attn_dense(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                      H, L, d, _dtype_code(q), out.data_ptr(),
+                                                      _stream_ptr(stream, q.device)))
+    return out
+
+
+def unpack_mask(mask, N):
+    """[H][N][W] int32 bit words -> [H][N][N] uint8 (host numpy)."""
+    import numpy as np
+    m = mask.cpu().numpy().view(np.uint32)
+    bits = np.unpackbits(m.view(np.uint8), axis=-1, bitorder="little")
+    return bits[..., :N].astype(np.uint8)

@@ -1,0 +1,171 @@
+// sol_api.hip -- C ABI of libsol.so (declared in include/sol.h).
+//
+// Host side only: argument validation, workspace carving and kernel launches
+// on the caller's stream.  No allocation, no synchronisation, no state kept
+// between calls.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "sol.h"
+#include "sol_launch.h"
+
+namespace {
+
+constexpr int kMaxBlocks = 8192;  // N bound: the proxy row lives in 32 KB of LDS
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(int H, int L, int d, int B) {
+    if (H < 1 || L < 1 || d < 1 || B < 1) return SOL_EINVAL;
+    if (d != 64 && d != 128) return SOL_EUNSUPPORTED;
+    if (B != 64 && B != 128) return SOL_EUNSUPPORTED;
+    const long long N = ((long long)L + B - 1) / B;
+    if (N > kMaxBlocks) return SOL_EUNSUPPORTED;
+    if ((long long)H * N > (1LL << 30)) return SOL_EUNSUPPORTED;
+    return SOL_OK;
+}
+
+int check_tensors(const void* q, const void* k, const void* v, const void* out, sol_dtype_t dt) {
+    if (dt != SOL_BF16 && dt != SOL_F32) return SOL_EINVAL;
+    if (!q || !k || !v || !out) return SOL_EINVAL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return SOL_EINVAL;
+    return SOL_OK;
+}
+
+struct Workspace {
+    float* qbar;
+    float* kbar;
+    float* vsum;
+    float* tau;
+    int* queues;
+    size_t bytes;
+};
+
+Workspace carve(void* base, int H, int L, int d, int B) {
+    const size_t N = ((size_t)L + B - 1) / B;
+    const size_t pooled = align_up(sizeof(float) * (size_t)H * N * d);
+    const size_t taub = align_up(sizeof(float) * (size_t)H * N);
+    const size_t qb = align_up(sizeof(int) * 8);
+    char* p = static_cast<char*>(base);
+    Workspace w;
+    w.qbar = reinterpret_cast<float*>(p);
+    w.kbar = reinterpret_cast<float*>(p + pooled);
+    w.vsum = reinterpret_cast<float*>(p + 2 * pooled);
+    w.tau = reinterpret_cast<float*>(p + 3 * pooled);
+    w.queues = reinterpret_cast<int*>(p + 3 * pooled + taub);
+    w.bytes = 3 * pooled + taub + qb;
+    return w;
+}
+
+int forward(const void* q, const void* k, const void* v, int H, int L, int d, int B, float beta,
+            sol_dtype_t dt, void* out, int32_t* kept, void* ws, size_t ws_bytes, void* stream,
+            uint32_t* sel_mask, float* tau_out) {
+    int st = check_shape(H, L, d, B);
+    if (st != SOL_OK) return st;
+    st = check_tensors(q, k, v, out, dt);
+    if (st != SOL_OK) return st;
+    if (!kept || !aligned(kept, 4) || isnan(beta)) return SOL_EINVAL;
+    if ((sel_mask && !aligned(sel_mask, 4)) || (tau_out && !aligned(tau_out, 4))) return SOL_EINVAL;
+    if (!ws || !aligned(ws, kAlign)) return SOL_EWORKSPACE;
+    const Workspace w = carve(ws, H, L, d, B);
+    if (ws_bytes < w.bytes) return SOL_EWORKSPACE;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int N = (L + B - 1) / B;
+    const int bf16 = dt == SOL_BF16;
+    const float c = static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
+    // The thresholds go straight to the caller's array when it asks for them.
+    float* tau = tau_out ? tau_out : w.tau;
+
+    if (sol::launch_pool(q, k, v, bf16, H, L, d, B, w.qbar, w.kbar, w.vsum, s) != hipSuccess)
+        return SOL_EHIP;
+    if (sol::launch_route(w.qbar, w.kbar, H, N, d, c, beta, tau, kept, w.queues, s) != hipSuccess)
+        return SOL_EHIP;
+    sol::AttnArgs a;
+    a.q = q; a.k = k; a.v = v;
+    a.qbar = w.qbar; a.kbar = w.kbar; a.vsum = w.vsum; a.tau = tau;
+    a.out = out;
+    a.sel_dbg = sel_mask;
+    a.queues = w.queues;
+    a.H = H; a.L = L; a.N = N; a.W = (N + 31) / 32;
+    a.nlast = L - (N - 1) * B;
+    a.c = c;
+    a.c_log2e = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(d)));
+    if (sol::launch_attn(a, bf16, d, B, false, s) != hipSuccess) return SOL_EHIP;
+    return SOL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sol_workspace_bytes(int H, int L, int d, int B) {
+    if (check_shape(H, L, d, B) != SOL_OK) return 0;
+    return carve(nullptr, H, L, d, B).bytes;
+}
+
+int sol_pool(const void* q, const void* k, const void* v, int H, int L, int d, int B, sol_dtype_t dt,
+             float* qbar, float* kbar, float* vsum, void* stream) {
+    int st = check_shape(H, L, d, B);
+    if (st != SOL_OK) return st;
+    if (dt != SOL_BF16 && dt != SOL_F32) return SOL_EINVAL;
+    if (!q || !k || !v || !qbar || !kbar || !vsum) return SOL_EINVAL;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(qbar, 4) ||
+        !aligned(kbar, 4) || !aligned(vsum, 4))
+        return SOL_EINVAL;
+    if (sol::launch_pool(q, k, v, dt == SOL_BF16, H, L, d, B, qbar, kbar, vsum,
+                         static_cast<hipStream_t>(stream)) != hipSuccess)
+        return SOL_EHIP;
+    return SOL_OK;
+}
+
+int sol_attn_fwd(const void* q, const void* k, const void* v, int H, int L, int d, int B, float beta,
+                 sol_dtype_t dt, void* out, int32_t* kept_counts, void* workspace, size_t ws_bytes,
+                 void* stream) {
+    return forward(q, k, v, H, L, d, B, beta, dt, out, kept_counts, workspace, ws_bytes, stream,
+                   nullptr, nullptr);
+}
+
+int sol_attn_fwd_dbg(const void* q, const void* k, const void* v, int H, int L, int d, int B,
+                     float beta, sol_dtype_t dt, void* out, int32_t* kept_counts, void* workspace,
+                     size_t ws_bytes, void* stream, uint32_t* sel_mask, float* tau) {
+    return forward(q, k, v, H, L, d, B, beta, dt, out, kept_counts, workspace, ws_bytes, stream,
+                   sel_mask, tau);
+}
+
+int sol_attn_dense(const void* q, const void* k, const void* v, int H, int L, int d, sol_dtype_t dt,
+                   void* out, void* stream) {
+    const int B = 64;
+    int st = check_shape(H, L, d, B);
+    if (st != SOL_OK) return st;
+    st = check_tensors(q, k, v, out, dt);
+    if (st != SOL_OK) return st;
+    const int N = (L + B - 1) / B;
+    sol::AttnArgs a = {};
+    a.q = q; a.k = k; a.v = v;
+    a.out = out;
+    a.H = H; a.L = L; a.N = N; a.W = (N + 31) / 32;
+    a.nlast = L - (N - 1) * B;
+    a.c = static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
+    a.c_log2e = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(d)));
+    if (sol::launch_attn(a, dt == SOL_BF16, d, B, true, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return SOL_EHIP;
+    return SOL_OK;
+}
+
+const char* sol_status_string(int status) {
+    switch (status) {
+        case SOL_OK: return "success";
+        case SOL_EINVAL: return "invalid argument (null or misaligned pointer, bad size, NaN beta or bad dtype)";
+        case SOL_EUNSUPPORTED: return "unsupported shape (d and B must be 64 or 128; N <= 8192)";
+        case SOL_EWORKSPACE: return "workspace missing, misaligned or smaller than sol_workspace_bytes()";
+        case SOL_EHIP: return "HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

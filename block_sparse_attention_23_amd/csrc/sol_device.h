@@ -1,0 +1,90 @@
+// sol_device.h -- device helpers shared by the Sol-Attn kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sol {
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_bits_to_f32(u16 b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (inputs here are finite).
+__device__ __forceinline__ u16 f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<u16>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16_bits(lo)) |
+           (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+}
+
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16) on one wavefront.
+// Lane l supplies A[l%16][8*(l/16) .. +8) and B[8*(l/16) .. +8)[l%16];
+// it receives D[4*(l/16) + r][l%16] in element r.
+__device__ __forceinline__ f32x4_t mfma16(const bf16x8_t& a, const bf16x8_t& b, const f32x4_t& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
+    return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ float wave_max_xor16_32(float x) {
+    x = fmaxf(x, __shfl_xor(x, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum_xor16_32(float x) {
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+// ---------------------------------------------------------------------------
+// Proxy score s_ij = qbar_i . kbar_j / sqrt(d) ("Sol-Attn" visual explainer,
+// Eq. (11) right-hand side), computed by four consecutive lanes: lane quarter
+// qq sums d/4 products in index order with fused multiply-adds, then the
+// quarters are combined as (p0 + p1) + (p2 + p3).  The routing kernel and the
+// attention kernel both call exactly these two functions with the same
+// operands, so both see bit-identical scores and take identical decisions.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void load_kbar_quarter(const float* __restrict__ row, int qq,
+                                                  float (&kv)[D / 4]) {
+    const float4* p = reinterpret_cast<const float4*>(row + qq * (D / 4));
+#pragma unroll
+    for (int e = 0; e < D / 16; ++e) {
+        float4 t = p[e];
+        kv[4 * e + 0] = t.x;
+        kv[4 * e + 1] = t.y;
+        kv[4 * e + 2] = t.z;
+        kv[4 * e + 3] = t.w;
+    }
+}
+
+template <int D>
+__device__ __forceinline__ float proxy_from_quarter(const float* qbar_lds, const float (&kv)[D / 4],
+                                                    int qq, float scale) {
+    const float* qp = qbar_lds + qq * (D / 4);
+    float acc = 0.0f;
+#pragma unroll
+    for (int e = 0; e < D / 4; ++e) acc = __builtin_fmaf(qp[e], kv[e], acc);
+    const float s01 = acc + __shfl_xor(acc, 1);
+    const float s = s01 + __shfl_xor(s01, 2);
+    return s * scale;
+}
+
+}  // namespace sol

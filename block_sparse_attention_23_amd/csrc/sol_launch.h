@@ -1,0 +1,33 @@
+// sol_launch.h -- host-side launchers of the Sol-Attn kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sol {
+
+struct AttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* qbar;   // [H][N][d] fp32 (unused by dense)
+    const float* kbar;
+    const float* vsum;
+    const float* tau;    // [H][N] fp32 (unused by dense)
+    void* out;
+    uint32_t* sel_dbg;   // [H][N][W] or null
+    int* queues;         // 8 per-XCD work counters (sol only)
+    int H, L, N, W;
+    int nlast;           // valid tokens in the last block
+    float c;             // 1/sqrt(d): proxy-score scale
+    float c_log2e;       // 1/sqrt(d) * log2(e): attention logits in base 2
+};
+
+// Each returns hipSuccess or the launch error.
+hipError_t launch_pool(const void* q, const void* k, const void* v, int bf16, int H, int L,
+                       int d, int B, float* qbar, float* kbar, float* vsum, hipStream_t s);
+hipError_t launch_route(const float* qbar, const float* kbar, int H, int N, int d, float c,
+                        float beta, float* tau, int32_t* kept, int* queues, hipStream_t s);
+hipError_t launch_attn(const AttnArgs& a, int bf16, int d, int B, bool dense, hipStream_t s);
+
+}  // namespace sol

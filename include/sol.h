@@ -1,0 +1,125 @@
+/*
+ * sol.h -- C ABI of the Sol-Attn library for MI355X (gfx950), libsol.so.
+ *
+ * Sol-Attn ("Sol-Attn: Accelerating Video Generation Inference via On-the-Fly
+ * Attention Sparsification"; abstract and the "Sol-Attn" visual paper
+ * explainer) computes block-sparse attention in one online-softmax sweep:
+ * pool Q, K and V into blocks; compare each pooled-key proxy score with a
+ * per-query-block threshold tau = mu + beta*sigma; compute selected key
+ * blocks exactly and fold every unselected block in as one pooled key that
+ * stands for its tokens, with their summed values.
+ *
+ * Conventions shared by every entry point:
+ *  - Token tensors q, k, v, out are DEVICE pointers to [H][L][d] row-major,
+ *    contiguous arrays of `dt` elements (bf16 or fp32), 16-byte aligned.
+ *    The caller owns all memory; the library allocates nothing.
+ *  - Blocks are B consecutive tokens; N = ceil(L / B); the last block holds
+ *    n_last = L - (N-1)*B valid tokens and is masked, never padded.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call is
+ *    asynchronous on that stream: it validates its arguments on the host,
+ *    enqueues kernels and returns.  Device-side faults surface at the
+ *    caller's next synchronisation of the stream.
+ *  - Return value: SOL_OK, or a negative sol_status_t.  Argument errors are
+ *    detected before anything is enqueued, and nothing is written then.
+ *  - Supported shapes: d in {64, 128}, B in {64, 128}, H >= 1, 1 <= L and
+ *    N <= 8192; anything else returns SOL_EUNSUPPORTED.
+ *  - Calls that share a workspace must be ordered on one stream; concurrent
+ *    calls need distinct workspaces.
+ */
+#ifndef SOL_H
+#define SOL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SOL_BF16 = 0, SOL_F32 = 1 } sol_dtype_t;
+
+typedef enum {
+    SOL_OK = 0,
+    SOL_EINVAL = -1,        /* null pointer, non-positive size, NaN beta, bad dtype */
+    SOL_EUNSUPPORTED = -2,  /* d, B or N outside the supported set */
+    SOL_EWORKSPACE = -3,    /* workspace missing or smaller than sol_workspace_bytes */
+    SOL_EHIP = -4           /* a HIP launch or query failed */
+} sol_status_t;
+
+/*
+ * Bytes of device workspace sol_attn_fwd / sol_attn_fwd_dbg need for this
+ * shape: the pooled tensors (3 x H*N*d fp32), the per-query-block thresholds
+ * (H*N fp32) and the scheduler's queue counters.  0 for invalid shapes.
+ */
+size_t sol_workspace_bytes(int H, int L, int d, int B);
+
+/*
+ * Block pooling ("Sol-Attn" visual explainer, "Pool Q, K and V into blocks";
+ * Eq. (5) legend: the mean query and key vector of a block; Eq. (10) legend:
+ * the summed values).  For each head h and block j, over its n_j valid
+ * tokens:
+ *     qbar[h][j] = mean of q,  kbar[h][j] = mean of k,  vsum[h][j] = sum of v.
+ * qbar, kbar, vsum: DEVICE fp32 [H][N][d], written entirely.
+ */
+int sol_pool(const void* q, const void* k, const void* v,
+             int H, int L, int d, int B, sol_dtype_t dt,
+             float* qbar, float* kbar, float* vsum, void* stream);
+
+/*
+ * Sol-Attn forward ("Sol-Attn" visual explainer: Eq. (4) selection rule,
+ * Eq. (5) statistics over all N key blocks, Eq. (9) denominator, Eq. (10)
+ * numerator, Eq. (11) token-to-pooled-block tile; abstract: one
+ * online-softmax pass without materialising the proxy map).  For each head h
+ * and query block i:
+ *     s_ij  = qbar_i . kbar_j / sqrt(d)        for all key blocks j
+ *     tau_i = mu_i + beta * sigma_i            (population mean / std of s_i.)
+ *     S_i   = { j : s_ij > tau_i }             (strict; beta=-inf: all, +inf: none)
+ * and for every query token r of block i, with a = q_r.k_t/sqrt(d) for keys
+ * t of selected blocks and g_j = q_r.kbar_j/sqrt(d) for unselected blocks j:
+ *     out_r = (sum_{j in U} e^{g_j} vsum_j + sum_{S} sum_t e^{a} v_t)
+ *           / (sum_{j in U} n_j e^{g_j}   + sum_{S} sum_t e^{a})
+ * Proxy scores exist only on chip; they are never written to memory.
+ *
+ * beta        : any float except NaN (+-INFINITY allowed).
+ * out         : DEVICE [H][L][d], dtype dt.
+ * kept_counts : DEVICE int32 [H][N], |S_i| for every (h, i).
+ * workspace   : DEVICE, at least sol_workspace_bytes(H, L, d, B) bytes,
+ *               256-byte aligned; contents are scratch (no state is kept
+ *               between calls).
+ */
+int sol_attn_fwd(const void* q, const void* k, const void* v,
+                 int H, int L, int d, int B, float beta, sol_dtype_t dt,
+                 void* out, int32_t* kept_counts,
+                 void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sol_attn_fwd plus diagnostics, for parity checks (never in timed runs):
+ * sel_mask : DEVICE uint32 [H][N][ceil(N/32)] or NULL; bit (j % 32) of word
+ *            j / 32 of row (h, i) is 1 iff key block j was computed exactly.
+ *            These are the decisions the attention kernel itself took.
+ * tau      : DEVICE fp32 [H][N] or NULL; the thresholds tau_i used.
+ */
+int sol_attn_fwd_dbg(const void* q, const void* k, const void* v,
+                     int H, int L, int d, int B, float beta, sol_dtype_t dt,
+                     void* out, int32_t* kept_counts,
+                     void* workspace, size_t ws_bytes, void* stream,
+                     uint32_t* sel_mask, float* tau);
+
+/*
+ * Dense softmax attention softmax(Q K^T / sqrt(d)) V (the pages' speedup
+ * baseline, "Sol-Attn" visual explainer, "What the paper measured": dense
+ * attention wall time over the method's), on the same tile machinery with
+ * every key block computed exactly.  out: DEVICE [H][L][d], dtype dt.
+ * Needs no workspace.  d in {64, 128}.
+ */
+int sol_attn_dense(const void* q, const void* k, const void* v,
+                   int H, int L, int d, sol_dtype_t dt, void* out, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* sol_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SOL_H */

@@ -1,0 +1,108 @@
+"""Parity helpers: run the HIP path through the C ABI and judge it against the
+fp64 oracle on the same seeded inputs.
+
+Judging rule (spec tolerances, readings of the pages recorded with the
+oracle):
+  * selection: the kernel's exact/approximate decision per (h, i, j) equals
+    the oracle's, except where |s_ij - tau_i| < 1e-3 in the oracle's values
+    (fp32 vs fp64 rounding at the threshold); such flips are counted;
+  * kept_counts equals the popcount of the kernel's own decisions;
+  * output: compared with the oracle's merge recomputed with the kernel's own
+    selection, element by element: bf16 max|err| <= 2e-2 and mean|err| <= 2e-3;
+    fp32 max|err| <= 1e-5.
+"""
+import numpy as np
+import torch
+
+import oracle
+from block_sparse_attention_23_amd import binding
+
+FLIP_BAND = 1e-3
+TOL = {"bf16": (2e-2, 2e-3), "fp32": (1e-5, 1e-5)}
+
+
+def to_device(inp, heads=None):
+    hs = slice(None) if heads is None else heads
+    if inp.workload.dtype == "bf16":
+        return [torch.from_numpy(np.ascontiguousarray(b[hs]).view(np.int16)).view(torch.bfloat16).cuda()
+                for b in (inp.q_bits, inp.k_bits, inp.v_bits)]
+    return [torch.from_numpy(np.ascontiguousarray(a[hs])).cuda() for a in (inp.q, inp.k, inp.v)]
+
+
+def block_rows(L, B, blocks):
+    """(h, r) rows of the listed (h, i) query blocks."""
+    rows = []
+    for h, i in blocks:
+        for r in range(i * B, min(L, (i + 1) * B)):
+            rows.append((h, r))
+    return np.array(rows, dtype=np.int32).reshape(-1, 2)
+
+
+def check_selection(q, k, v, B, beta, gsel, gkept, heads=None):
+    """Selection parity with the flip rule.  q, k, v: float32 host arrays of
+    the heads compared (all heads when `heads` is None).  Returns
+    (flips, oracle kept fraction, pooled tensors)."""
+    qbar, kbar, vsum = oracle.pool(q, k, v, B)
+    H = q.shape[0]
+    flips = 0
+    okept = 0
+    for h in range(H):
+        r = oracle.route(qbar[h:h + 1], kbar[h:h + 1], beta, want_shat=True)
+        g = gsel[h]
+        mism = g != r["sel"][0]
+        okept += int(r["kept"].sum())
+        if mism.any():
+            dist = np.abs(r["shat"][0] - r["tau"][0][:, None])
+            bad = mism & ~(dist < FLIP_BAND)
+            assert not bad.any(), (
+                f"head {h}: {int(bad.sum())} selection mismatches outside the flip band; "
+                f"first at (i, j) = {tuple(np.argwhere(bad)[0])}")
+            flips += int(mism.sum())
+    assert np.array_equal(gkept.astype(np.int64), gsel.sum(-1).astype(np.int64)), \
+        "kept_counts differ from the kernel's own decisions"
+    N = gsel.shape[-1]
+    return flips, okept / (H * N * N), (qbar, kbar, vsum)
+
+
+def judge_output(got, ref, dtype):
+    tmax, tmean = TOL[dtype]
+    err = np.abs(got.astype(np.float64) - ref)
+    stats = {"max_err": float(err.max()), "mean_err": float(err.mean())}
+    assert np.all(np.isfinite(got)), "non-finite output"
+    assert stats["max_err"] <= tmax and stats["mean_err"] <= tmean, stats
+    return stats
+
+
+def _take(a, hs):
+    return a if hs == list(range(a.shape[0])) else a[hs]
+
+
+def run_and_check(inp, B, beta, rows=None, sel_heads=None):
+    """Full check of sol_attn_fwd_dbg on `inp` (all heads run on the GPU).
+
+    rows: None = compare every output row; else an [n][2] array of (h, r)
+    with h indexing `sel_heads` (or all heads).
+    sel_heads: heads whose selection and outputs are checked (None = all)."""
+    w = inp.workload
+    q, k, v = to_device(inp)
+    out, kept, mask, tau = binding.attn_fwd(q, k, v, B, beta, debug=True)
+    torch.cuda.synchronize()
+    H, L, d = q.shape
+    N = (L + B - 1) // B
+    gsel = binding.unpack_mask(mask, N)
+    gkept = kept.cpu().numpy()
+    hs = list(range(H)) if sel_heads is None else list(sel_heads)
+    qh, kh, vh = _take(inp.q, hs), _take(inp.k, hs), _take(inp.v, hs)
+    flips, okept, (qbar, kbar, vsum) = check_selection(qh, kh, vh, B, beta, _take(gsel, hs),
+                                                       _take(gkept, hs))
+    if rows is None:
+        ref = oracle.merge(qh, kh, vh, kbar, vsum, B, _take(gsel, hs))
+        got = out[hs].float().cpu().numpy()
+    else:
+        ref = oracle.merge(qh, kh, vh, kbar, vsum, B, _take(gsel, hs), rows=rows)
+        hidx = torch.tensor([hs[h] for h in rows[:, 0]], device=out.device, dtype=torch.long)
+        ridx = torch.tensor(rows[:, 1], device=out.device, dtype=torch.long)
+        got = out[hidx, ridx].float().cpu().numpy()
+    stats = judge_output(got, ref, w.dtype)
+    stats.update(flips=flips, kept_frac=float(gsel.mean()), oracle_kept_frac=okept)
+    return stats

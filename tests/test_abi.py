@@ -1,0 +1,113 @@
+"""The C ABI without a GPU: libsol.so loads, exports every function that
+include/sol.h declares, sizes workspaces, and rejects bad arguments on the
+host before anything is enqueued (no kernel runs in these tests)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_23_amd import binding, build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sol.h")
+
+FAKE = 0x10000  # 16-byte-aligned non-null address; validation fails before any use
+FAKE_WS = 0x100000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sol_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(build.LIB):
+        build.build()
+    return binding.lib()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "sol_attn_dense", "sol_attn_fwd", "sol_attn_fwd_dbg", "sol_pool",
+        "sol_status_string", "sol_workspace_bytes"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(build.LIB)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4):
+        assert binding.status_string(st)
+    assert binding.status_string(7) == "unknown status"
+
+
+def test_workspace_bytes(lib):
+    H, L, d, B = 40, 75600, 128, 64
+    N = 1182
+    n = binding.workspace_bytes(H, L, d, B)
+    assert n >= 3 * H * N * d * 4 + H * N * 4
+    assert n % 256 == 0
+    assert binding.workspace_bytes(1, 1, 64, 64) > 0
+    for bad in [(0, 10, 64, 64), (1, 0, 64, 64), (1, 10, 96, 64), (1, 10, 64, 32),
+                (1, 8192 * 64 + 1, 64, 64)]:
+        assert binding.workspace_bytes(*bad) == 0
+
+
+def _fwd(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, H=2, L=100, d=64, B=64, beta=1.0, dt=0, out=FAKE,
+             kept=FAKE, ws=FAKE_WS, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return lib.sol_attn_fwd(a["q"], a["k"], a["v"], a["H"], a["L"], a["d"], a["B"], a["beta"],
+                            a["dt"], a["out"], a["kept"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_forward_rejects_bad_arguments_before_launch(lib):
+    assert _fwd(lib, q=None) == -1
+    assert _fwd(lib, out=None) == -1
+    assert _fwd(lib, kept=None) == -1
+    assert _fwd(lib, H=0) == -1
+    assert _fwd(lib, L=-5) == -1
+    assert _fwd(lib, d=96) == -2
+    assert _fwd(lib, B=32) == -2
+    assert _fwd(lib, L=8192 * 64 + 1) == -2
+    assert _fwd(lib, beta=math.nan) == -1
+    assert _fwd(lib, dt=5) == -1
+    assert _fwd(lib, q=FAKE + 2) == -1          # misaligned
+    assert _fwd(lib, ws=None) == -3
+    assert _fwd(lib, ws=FAKE_WS + 16) == -3     # workspace must be 256-byte aligned
+    assert _fwd(lib, ws_bytes=16) == -3
+
+
+def test_pool_and_dense_reject_bad_arguments(lib):
+    assert lib.sol_pool(FAKE, FAKE, None, 1, 10, 64, 64, 0, FAKE, FAKE, FAKE, None) == -1
+    assert lib.sol_pool(FAKE, FAKE, FAKE, 1, 10, 64, 48, 0, FAKE, FAKE, FAKE, None) == -2
+    assert lib.sol_attn_dense(FAKE, FAKE, FAKE, 1, 10, 80, 0, FAKE, None) == -2
+    assert lib.sol_attn_dense(FAKE, None, FAKE, 1, 10, 64, 0, FAKE, None) == -1
+    assert lib.sol_attn_dense(FAKE, FAKE, FAKE, 1, 10, 64, 3, FAKE, None) == -1
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(1, 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        binding.attn_fwd(x, x, x, 64, 1.0)
+    with pytest.raises(ValueError):
+        binding.attn_dense(x, x, x)
+
+
+def test_unpack_mask_bit_order():
+    import numpy as np
+    import torch
+    m = torch.tensor([[[0b1011, 1 << 31]]], dtype=torch.int64).to(torch.int32)
+    bits = binding.unpack_mask(m, 33)
+    assert bits.shape == (1, 1, 33)
+    assert list(np.nonzero(bits[0, 0])[0]) == [0, 1, 3]
+    m2 = torch.tensor([[[0, 1]]], dtype=torch.int32)
+    assert list(np.nonzero(binding.unpack_mask(m2, 40)[0, 0])[0]) == [32]
