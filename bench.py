@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Sol-Attn benchmark on one MI355X (gfx950).
+
+Workload: the Wan-2.1-14B-shaped attention layer -- 40 heads, a 21x45x80
+latent grid (L = 75,600 tokens, ragged last block of 16), d = 128, B = 64,
+bf16, synthetic locality-structured Q/K/V (seed 2) -- at beta = 1.0, then the
+beta sweep {0.5, 1.5, 2.0}.  One step = one sol_attn_fwd call (pool, route
+and the fused sweep) on inputs already resident in HBM.
+
+Prints one JSON line on stdout: dense-equivalent TFLOP/s (4 H L^2 d / step
+time) as `value`, the sweep kernel's roofline (algorithmic FLOPs per launch /
+its HIP-event-timed duration), kept-block fraction, the in-library dense
+baseline, and the fp64 CPU oracle timed on a bounded sample as a baseline.
+Progress goes to stderr.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_c3_beta1_pmc.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="C3")
+    ap.add_argument("--betas", default=None,
+                    help="comma-separated betas; the first is the headline (default: 1.0 then "
+                         "the workload's sweep)")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_attention_23_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per sweep launch from the committed PMC summary, if it was
+    taken on the current kernel sources (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_digest") != source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def time_loop(fn, steps, warmup, torch):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(steps):
+        fn()
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def cpu_baseline(w, inp_head0, beta, target_s):
+    """The fp64 oracle on a bounded sample: head 0 (pool + route of the whole
+    head, then the merge for the first n query blocks)."""
+    import numpy as np
+    import oracle
+    q, k, v = inp_head0
+    B, L, d = w.B, w.L, w.d
+    t0 = time.perf_counter()
+    qbar, kbar, vsum = oracle.pool(q, k, v, B)
+    r = oracle.route(qbar, kbar, beta)
+    t_prep = time.perf_counter() - t0
+
+    def merge_blocks(n):
+        rows = np.array([(0, x) for x in range(min(L, n * B))], dtype=np.int32)
+        t = time.perf_counter()
+        oracle.merge(q, k, v, kbar, vsum, B, r["sel"], rows=rows)
+        return time.perf_counter() - t
+
+    t1 = merge_blocks(2) / 2
+    n = max(2, min(w.N, int(max(1.0, target_s - t_prep) / max(t1, 1e-6))))
+    t_merge = merge_blocks(n)
+    total = t_prep + t_merge
+    flops = n * B * 4.0 * L * d
+    return {
+        "value": flops / total / 1e12, "unit": "dense-equiv TFLOP/s", "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": (f"{w.name} head 0 at beta={beta}: pool + route of the whole head, merge of the "
+                   f"first {n} query blocks ({n * B} rows) = {flops / 1e12:.3f} dense-equiv "
+                   f"TFLOP in {total:.1f} s"),
+        "seconds": total,
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from block_sparse_attention_23_amd import binding
+    from block_sparse_attention_23_amd import inputs as gen
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    binding.lib()
+    w = gen.WORKLOADS[args.workload]
+    betas = ([float(b) for b in args.betas.split(",")] if args.betas else
+             [1.0] + [b for b in w.betas if b != 1.0])
+    H, L, d, B, N = w.H, w.L, w.d, w.B, w.N
+    log(f"[bench] generating {w.name}: {w.desc}")
+    t = time.perf_counter()
+    inp = gen.generate(w)
+    log(f"[bench] generated in {time.perf_counter() - t:.1f}s")
+    if w.dtype == "bf16":
+        dev = [torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+               for b in (inp.q_bits, inp.k_bits, inp.v_bits)]
+    else:
+        dev = [torch.from_numpy(a).cuda() for a in (inp.q, inp.k, inp.v)]
+    q, k, v = dev
+    head0 = (inp.q[:1].copy(), inp.k[:1].copy(), inp.v[:1].copy())
+    del inp
+    out = torch.empty_like(q)
+    kept = torch.empty((H, N), dtype=torch.int32, device="cuda")
+    ws = binding.alloc_workspace(H, L, d, B, "cuda")
+    torch.cuda.synchronize()
+
+    F_dense = w.dense_flops
+    results = []
+    for beta in betas:
+        fn = lambda: binding.attn_fwd(q, k, v, B, beta, out=out, kept=kept, workspace=ws)
+        ms, wall = time_loop(fn, args.steps, args.warmup, torch)
+        kc = kept.to(torch.int64)
+        n_sel = int(kc.sum().item())
+        n_unsel = H * N * N - n_sel
+        F_exact = n_sel * 4.0 * B * B * d
+        F_approx = n_unsel * 4.0 * B * d
+        results.append(dict(beta=beta, ms=ms, wall_s=wall, kept_frac=n_sel / (H * N * N),
+                            F_exact=F_exact, F_approx=F_approx,
+                            tflops_dense_eq=F_dense / (ms * 1e-3) / 1e12))
+        log(f"[bench] beta={beta}: {ms:.3f} ms/step, kept {n_sel / (H * N * N):.4f}, "
+            f"{F_dense / (ms * 1e-3) / 1e12:.1f} dense-equiv TFLOP/s")
+    head = results[0]
+
+    # Stage breakdown at the headline beta: the same three kernels launched
+    # through the stage entry points, with HIP events between them.
+    qbar = torch.empty((H, N, d), dtype=torch.float32, device="cuda")
+    kbar, vsum = torch.empty_like(qbar), torch.empty_like(qbar)
+    tau = torch.empty((H, N), dtype=torch.float32, device="cuda")
+    counters = torch.empty(8, dtype=torch.int32, device="cuda")
+    beta0 = head["beta"]
+    s = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for it in range(args.warmup + args.steps):
+        e = ev[it - args.warmup] if it >= args.warmup else None
+        if e: e[0].record(s)
+        binding.pool(q, k, v, B, outs=(qbar, kbar, vsum))
+        if e: e[1].record(s)
+        binding.route(qbar, kbar, L, B, beta0, tau=tau, kept=kept)
+        if e: e[2].record(s)
+        binding.sweep(q, k, v, qbar, kbar, vsum, tau, B, out=out, counters=counters)
+        if e: e[3].record(s)
+    torch.cuda.synchronize()
+    st = {"pool": 0.0, "route": 0.0, "sweep": 0.0}
+    for e in ev:
+        st["pool"] += e[0].elapsed_time(e[1]) / args.steps
+        st["route"] += e[1].elapsed_time(e[2]) / args.steps
+        st["sweep"] += e[2].elapsed_time(e[3]) / args.steps
+    log(f"[bench] stages at beta={beta0}: " + ", ".join(f"{k} {v:.3f} ms" for k, v in st.items()))
+    F_alg = head["F_exact"] + head["F_approx"]
+    achieved = F_alg / (st["sweep"] * 1e-3) / 1e12
+    pool_bytes = 3.0 * H * L * d * (2 if w.dtype == "bf16" else 4) + 3.0 * H * N * d * 4
+    traffic = measured_traffic()
+
+    dense = None
+    if not args.no_dense:
+        fn = lambda: binding.attn_dense(q, k, v, out=out)
+        dms, _ = time_loop(fn, max(2, args.steps // 2), 1, torch)
+        dt = F_dense / (dms * 1e-3) / 1e12
+        dense = {"ms": dms, "tflops": dt, "mfma_util": dt / PEAK_BF16_TFLOPS}
+        log(f"[bench] dense: {dms:.3f} ms, {dt:.1f} TFLOP/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(w, head0, beta0, args.cpu_seconds)
+        log(f"[bench] oracle: {cpu['sample']} ({cpu['cores']} threads)")
+
+    line = {
+        "metric": "dense-equiv attn TFLOPS + MFMA util at L=75.6K,d=128 vs beta; kept-block %",
+        "value": head["tflops_dense_eq"],
+        "unit": "TFLOP/s (dense-equivalent, 4*H*L^2*d / step time)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded locality-structured Fourier-feature Q/K, N(0,1) V)",
+        "config": {"workload": f"{w.name}: {w.desc}", "H": H, "L": L, "d": d, "B": B,
+                   "N": N, "beta": head["beta"], "seed": w.seed},
+        "kept_block_frac": head["kept_frac"],
+        "exact_tile_mfma_util": head["F_exact"] / (st["sweep"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": traffic, "kernel": "sweep (attn_bf16_kernel<128,64,false>)",
+                     "algorithmic_flop_per_launch": F_alg},
+        "stage_ms": st,
+        "pool_gbs": pool_bytes / (st["pool"] * 1e-3) / 1e9,
+        "dense_baseline": dense,
+        "speedup_vs_dense": (dense["ms"] / head["ms"]) if dense else None,
+        "beta_sweep": [{"beta": r["beta"], "ms": r["ms"], "kept_frac": r["kept_frac"],
+                        "tflops_dense_eq": r["tflops_dense_eq"]} for r in results],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

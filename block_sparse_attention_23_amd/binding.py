@@ -18,6 +18,10 @@ _FUNCS = {
     "sol_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
     "sol_pool": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 5
                  + [ctypes.c_void_p] * 4),
+    "sol_route": (ctypes.c_int, [ctypes.c_void_p] * 2 + [ctypes.c_int] * 4
+                  + [ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "sol_sweep": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 5
+                  + [ctypes.c_void_p] * 4),
     "sol_attn_fwd": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4
                      + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
@@ -109,16 +113,50 @@ def alloc_workspace(H, L, d, B, device):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def pool(q, k, v, B, stream=None):
+def pool(q, k, v, B, outs=None, stream=None):
     """Block means of q and k and block sums of v, fp32 [H][N][d]."""
     H, L, d = _tokens(q, k, v)
     N = nblocks(L, B)
-    outs = [torch.empty((H, N, d), dtype=torch.float32, device=q.device) for _ in range(3)]
+    if outs is None:
+        outs = [torch.empty((H, N, d), dtype=torch.float32, device=q.device) for _ in range(3)]
     with torch.cuda.device(q.device):
         _check("sol_pool", lib().sol_pool(q.data_ptr(), k.data_ptr(), v.data_ptr(), H, L, d, B,
                                           _dtype_code(q), outs[0].data_ptr(), outs[1].data_ptr(),
                                           outs[2].data_ptr(), _stream_ptr(stream, q.device)))
     return tuple(outs)
+
+
+def route(qbar, kbar, L, B, beta, tau=None, kept=None, stream=None):
+    """Thresholds tau [H][N] and kept counts [H][N] from pooled tensors."""
+    H, N, d = qbar.shape
+    if not (qbar.is_cuda and kbar.is_cuda):
+        raise ValueError("pooled tensors must live on the GPU")
+    if tau is None:
+        tau = torch.empty((H, N), dtype=torch.float32, device=qbar.device)
+    if kept is None:
+        kept = torch.empty((H, N), dtype=torch.int32, device=qbar.device)
+    with torch.cuda.device(qbar.device):
+        _check("sol_route", lib().sol_route(qbar.data_ptr(), kbar.data_ptr(), H, L, d, B,
+                                            float(beta), tau.data_ptr(), kept.data_ptr(),
+                                            _stream_ptr(stream, qbar.device)))
+    return tau, kept
+
+
+def sweep(q, k, v, qbar, kbar, vsum, tau, B, out=None, counters=None, sel_mask=None,
+          stream=None):
+    """The fused exact/approximate sweep given pooled tensors and thresholds."""
+    H, L, d = _tokens(q, k, v)
+    if out is None:
+        out = torch.empty_like(q)
+    if counters is None:
+        counters = torch.empty(8, dtype=torch.int32, device=q.device)
+    with torch.cuda.device(q.device):
+        _check("sol_sweep", lib().sol_sweep(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), qbar.data_ptr(), kbar.data_ptr(),
+            vsum.data_ptr(), tau.data_ptr(), H, L, d, B, _dtype_code(q), out.data_ptr(),
+            counters.data_ptr(), None if sel_mask is None else sel_mask.data_ptr(),
+            _stream_ptr(stream, q.device)))
+    return out
 
 
 def attn_fwd(q, k, v, B, beta, out=None, kept=None, workspace=None, stream=None, debug=False):

@@ -61,6 +61,23 @@ Workspace carve(void* base, int H, int L, int d, int B) {
     return w;
 }
 
+sol::AttnArgs sweep_args(const void* q, const void* k, const void* v, const float* qbar,
+                         const float* kbar, const float* vsum, const float* tau, int H, int L, int d,
+                         int B, void* out, int* counters, uint32_t* sel_mask) {
+    const int N = (L + B - 1) / B;
+    sol::AttnArgs a = {};
+    a.q = q; a.k = k; a.v = v;
+    a.qbar = qbar; a.kbar = kbar; a.vsum = vsum; a.tau = tau;
+    a.out = out;
+    a.sel_dbg = sel_mask;
+    a.queues = counters;
+    a.H = H; a.L = L; a.N = N; a.W = (N + 31) / 32;
+    a.nlast = L - (N - 1) * B;
+    a.c = static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
+    a.c_log2e = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(d)));
+    return a;
+}
+
 int forward(const void* q, const void* k, const void* v, int H, int L, int d, int B, float beta,
             sol_dtype_t dt, void* out, int32_t* kept, void* ws, size_t ws_bytes, void* stream,
             uint32_t* sel_mask, float* tau_out) {
@@ -85,16 +102,8 @@ int forward(const void* q, const void* k, const void* v, int H, int L, int d, in
         return SOL_EHIP;
     if (sol::launch_route(w.qbar, w.kbar, H, N, d, c, beta, tau, kept, w.queues, s) != hipSuccess)
         return SOL_EHIP;
-    sol::AttnArgs a;
-    a.q = q; a.k = k; a.v = v;
-    a.qbar = w.qbar; a.kbar = w.kbar; a.vsum = w.vsum; a.tau = tau;
-    a.out = out;
-    a.sel_dbg = sel_mask;
-    a.queues = w.queues;
-    a.H = H; a.L = L; a.N = N; a.W = (N + 31) / 32;
-    a.nlast = L - (N - 1) * B;
-    a.c = c;
-    a.c_log2e = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(d)));
+    const sol::AttnArgs a = sweep_args(q, k, v, w.qbar, w.kbar, w.vsum, tau, H, L, d, B, out,
+                                       w.queues, sel_mask);
     if (sol::launch_attn(a, bf16, d, B, false, s) != hipSuccess) return SOL_EHIP;
     return SOL_OK;
 }
@@ -120,6 +129,40 @@ int sol_pool(const void* q, const void* k, const void* v, int H, int L, int d, i
     if (sol::launch_pool(q, k, v, dt == SOL_BF16, H, L, d, B, qbar, kbar, vsum,
                          static_cast<hipStream_t>(stream)) != hipSuccess)
         return SOL_EHIP;
+    return SOL_OK;
+}
+
+int sol_route(const float* qbar, const float* kbar, int H, int L, int d, int B, float beta,
+              float* tau, int32_t* kept_counts, void* stream) {
+    int st = check_shape(H, L, d, B);
+    if (st != SOL_OK) return st;
+    if (!qbar || !kbar || !tau || !kept_counts || isnan(beta)) return SOL_EINVAL;
+    if (!aligned(qbar, 16) || !aligned(kbar, 16) || !aligned(tau, 4) || !aligned(kept_counts, 4))
+        return SOL_EINVAL;
+    const int N = (L + B - 1) / B;
+    const float c = static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
+    if (sol::launch_route(qbar, kbar, H, N, d, c, beta, tau, kept_counts, nullptr,
+                          static_cast<hipStream_t>(stream)) != hipSuccess)
+        return SOL_EHIP;
+    return SOL_OK;
+}
+
+int sol_sweep(const void* q, const void* k, const void* v, const float* qbar, const float* kbar,
+              const float* vsum, const float* tau, int H, int L, int d, int B, sol_dtype_t dt,
+              void* out, int32_t* counters, uint32_t* sel_mask, void* stream) {
+    int st = check_shape(H, L, d, B);
+    if (st != SOL_OK) return st;
+    st = check_tensors(q, k, v, out, dt);
+    if (st != SOL_OK) return st;
+    if (!qbar || !kbar || !vsum || !tau || !counters) return SOL_EINVAL;
+    if (!aligned(qbar, 16) || !aligned(kbar, 16) || !aligned(vsum, 16) || !aligned(tau, 4) ||
+        !aligned(counters, 4) || (sel_mask && !aligned(sel_mask, 4)))
+        return SOL_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (sol::launch_reset_counters(counters, s) != hipSuccess) return SOL_EHIP;
+    const sol::AttnArgs a = sweep_args(q, k, v, qbar, kbar, vsum, tau, H, L, d, B, out, counters,
+                                       sel_mask);
+    if (sol::launch_attn(a, dt == SOL_BF16, d, B, false, s) != hipSuccess) return SOL_EHIP;
     return SOL_OK;
 }
 

@@ -124,9 +124,9 @@ __device__ __forceinline__ float block_sum256(float x, float* red4) {
 
 // One workgroup (256 threads) per (head h, query block i).  The proxy row
 // s_i. (N floats) lives in dynamic LDS only.  Writes tau_i and the kept
-// count |{j : s_ij > tau_i}|.  Workgroup 0 also resets the attention
-// kernel's eight work counters (this kernel always runs just before it on
-// the same stream).
+// count |{j : s_ij > tau_i}|.  When `queues` is given, workgroup 0 also
+// resets the sweep's eight work counters (the forward pass launches the
+// sweep right after this kernel on the same stream).
 template <int D>
 __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qbar,
                                                     const float* __restrict__ kbar, int N,
@@ -140,7 +140,7 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
     const int item = blockIdx.x;
     const int h = item / N;
     const int tid = threadIdx.x;
-    if (item == 0 && tid < 8) queues[tid] = 0;
+    if (queues && item == 0 && tid < 8) queues[tid] = 0;
     for (int t = tid; t < D; t += 256) qb[t] = qbar[(size_t)item * D + t];
     __syncthreads();
 
@@ -174,6 +174,10 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
         tau_out[item] = tau;
         kept[item] = static_cast<int32_t>(total);
     }
+}
+
+__global__ void reset_counters_kernel(int* queues) {
+    if (threadIdx.x < 8) queues[threadIdx.x] = 0;
 }
 
 // ============================================================================
@@ -770,6 +774,11 @@ hipError_t launch_route(const float* qbar, const float* kbar, int H, int N, int 
         hipLaunchKernelGGL(route_kernel<128>, grid, block, shm, s, qbar, kbar, N, c, beta, tau, kept, queues);
     else
         return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_reset_counters(int* queues, hipStream_t s) {
+    hipLaunchKernelGGL(reset_counters_kernel, dim3(1), dim3(64), 0, s, queues);
     return hipGetLastError();
 }
 

@@ -28,6 +28,7 @@ hipError_t launch_pool(const void* q, const void* k, const void* v, int bf16, in
                        int d, int B, float* qbar, float* kbar, float* vsum, hipStream_t s);
 hipError_t launch_route(const float* qbar, const float* kbar, int H, int N, int d, float c,
                         float beta, float* tau, int32_t* kept, int* queues, hipStream_t s);
+hipError_t launch_reset_counters(int* queues, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int bf16, int d, int B, bool dense, hipStream_t s);
 
 }  // namespace sol

@@ -66,6 +66,36 @@ int sol_pool(const void* q, const void* k, const void* v,
              float* qbar, float* kbar, float* vsum, void* stream);
 
 /*
+ * Routing statistics ("Sol-Attn" visual explainer, Eq. (4) and Eq. (5);
+ * Eq. (11) right-hand side for the proxy score).  For every (h, i):
+ *     s_ij  = qbar_i . kbar_j / sqrt(d)  for j = 0..N-1 (kept on chip only)
+ *     mu_i  = (1/N) sum_j s_ij,  sigma_i^2 = (1/N) sum_j (s_ij - mu_i)^2
+ *     tau_i = mu_i + beta * sigma_i      (beta = -inf / +inf -> tau = -inf / +inf)
+ *     kept_counts[h][i] = |{ j : s_ij > tau_i }|
+ * qbar, kbar : DEVICE fp32 [H][N][d] (as written by sol_pool).
+ * tau        : DEVICE fp32 [H][N], written.
+ * kept_counts: DEVICE int32 [H][N], written.
+ * The counts equal those of the sweep: both stages compute each s_ij with
+ * the same arithmetic.
+ */
+int sol_route(const float* qbar, const float* kbar, int H, int L, int d, int B,
+              float beta, float* tau, int32_t* kept_counts, void* stream);
+
+/*
+ * The fused sweep alone: given the pooled tensors and thresholds, for every
+ * (h, i) stream the pooled keys in chunks, recompute their proxy scores,
+ * route each key block (s_ij > tau_i: exact; otherwise approximate) and merge
+ * both paths into one online softmax ("Sol-Attn" visual explainer, Eq. (9),
+ * Eq. (10), Eq. (11); abstract).  Output as sol_attn_fwd.
+ * counters : DEVICE int32[8] scratch for the work queues (overwritten).
+ * sel_mask : as in sol_attn_fwd_dbg, or NULL.
+ */
+int sol_sweep(const void* q, const void* k, const void* v,
+              const float* qbar, const float* kbar, const float* vsum, const float* tau,
+              int H, int L, int d, int B, sol_dtype_t dt, void* out,
+              int32_t* counters, uint32_t* sel_mask, void* stream);
+
+/*
  * Sol-Attn forward ("Sol-Attn" visual explainer: Eq. (4) selection rule,
  * Eq. (5) statistics over all N key blocks, Eq. (9) denominator, Eq. (10)
  * numerator, Eq. (11) token-to-pooled-block tile; abstract: one
@@ -79,6 +109,7 @@ int sol_pool(const void* q, const void* k, const void* v,
  *     out_r = (sum_{j in U} e^{g_j} vsum_j + sum_{S} sum_t e^{a} v_t)
  *           / (sum_{j in U} n_j e^{g_j}   + sum_{S} sum_t e^{a})
  * Proxy scores exist only on chip; they are never written to memory.
+ * Equivalent to sol_pool, then sol_route, then sol_sweep on one stream.
  *
  * beta        : any float except NaN (+-INFINITY allowed).
  * out         : DEVICE [H][L][d], dtype dt.

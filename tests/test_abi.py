@@ -32,8 +32,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "sol_attn_dense", "sol_attn_fwd", "sol_attn_fwd_dbg", "sol_pool",
-        "sol_status_string", "sol_workspace_bytes"])
+        "sol_attn_dense", "sol_attn_fwd", "sol_attn_fwd_dbg", "sol_pool", "sol_route",
+        "sol_status_string", "sol_sweep", "sol_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -91,6 +91,22 @@ def test_pool_and_dense_reject_bad_arguments(lib):
     assert lib.sol_attn_dense(FAKE, FAKE, FAKE, 1, 10, 80, 0, FAKE, None) == -2
     assert lib.sol_attn_dense(FAKE, None, FAKE, 1, 10, 64, 0, FAKE, None) == -1
     assert lib.sol_attn_dense(FAKE, FAKE, FAKE, 1, 10, 64, 3, FAKE, None) == -1
+
+
+def test_stage_entry_points_reject_bad_arguments(lib):
+    assert lib.sol_route(FAKE, None, 1, 100, 64, 64, 1.0, FAKE, FAKE, None) == -1
+    assert lib.sol_route(FAKE, FAKE, 1, 100, 64, 64, math.nan, FAKE, FAKE, None) == -1
+    assert lib.sol_route(FAKE, FAKE, 1, 100, 64, 16, 1.0, FAKE, FAKE, None) == -2
+    args = [FAKE] * 7 + [1, 100, 64, 64, 0, FAKE, FAKE, None, None]
+    bad = list(args)
+    bad[13] = None  # counters
+    assert lib.sol_sweep(*bad) == -1
+    bad = list(args)
+    bad[6] = None  # tau
+    assert lib.sol_sweep(*bad) == -1
+    bad = list(args)
+    bad[9] = 96  # d
+    assert lib.sol_sweep(*bad) == -2
 
 
 def test_binding_refuses_cpu_tensors(lib):
