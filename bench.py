@@ -185,7 +185,6 @@ def main():
     qbar = torch.empty((H, N, d), dtype=torch.float32, device="cuda")
     kbar, vsum = torch.empty_like(qbar), torch.empty_like(qbar)
     tau = torch.empty((H, N), dtype=torch.float32, device="cuda")
-    counters = torch.empty(8, dtype=torch.int32, device="cuda")
     beta0 = head["beta"]
     s = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -196,7 +195,7 @@ def main():
         if e: e[1].record(s)
         binding.route(qbar, kbar, L, B, beta0, tau=tau, kept=kept)
         if e: e[2].record(s)
-        binding.sweep(q, k, v, qbar, kbar, vsum, tau, B, out=out, counters=counters)
+        binding.sweep(q, k, v, qbar, kbar, vsum, tau, B, out=out, workspace=ws)
         if e: e[3].record(s)
     torch.cuda.synchronize()
     st = {"pool": 0.0, "route": 0.0, "sweep": 0.0}
@@ -243,7 +242,7 @@ def main():
         "exact_tile_mfma_util": head["F_exact"] / (st["sweep"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic, "kernel": "sweep (attn_bf16_kernel<128,64,false>)",
+                     "traffic": traffic, "kernel": "sweep_bf16_kernel<128, 64, false>",
                      "algorithmic_flop_per_launch": F_alg},
         "stage_ms": st,
         "pool_gbs": pool_bytes / (st["pool"] * 1e-3) / 1e9,

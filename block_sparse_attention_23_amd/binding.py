@@ -21,7 +21,8 @@ _FUNCS = {
     "sol_route": (ctypes.c_int, [ctypes.c_void_p] * 2 + [ctypes.c_int] * 4
                   + [ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "sol_sweep": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 5
-                  + [ctypes.c_void_p] * 4),
+                  + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                     ctypes.c_void_p]),
     "sol_attn_fwd": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4
                      + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
@@ -142,20 +143,20 @@ def route(qbar, kbar, L, B, beta, tau=None, kept=None, stream=None):
     return tau, kept
 
 
-def sweep(q, k, v, qbar, kbar, vsum, tau, B, out=None, counters=None, sel_mask=None,
+def sweep(q, k, v, qbar, kbar, vsum, tau, B, out=None, workspace=None, sel_mask=None,
           stream=None):
     """The fused exact/approximate sweep given pooled tensors and thresholds."""
     H, L, d = _tokens(q, k, v)
     if out is None:
         out = torch.empty_like(q)
-    if counters is None:
-        counters = torch.empty(8, dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(H, L, d, B, q.device)
     with torch.cuda.device(q.device):
         _check("sol_sweep", lib().sol_sweep(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), qbar.data_ptr(), kbar.data_ptr(),
             vsum.data_ptr(), tau.data_ptr(), H, L, d, B, _dtype_code(q), out.data_ptr(),
-            counters.data_ptr(), None if sel_mask is None else sel_mask.data_ptr(),
-            _stream_ptr(stream, q.device)))
+            workspace.data_ptr(), workspace.numel(),
+            None if sel_mask is None else sel_mask.data_ptr(), _stream_ptr(stream, q.device)))
     return out
 
 

@@ -11,7 +11,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsol.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("sol_kernels.hip", "sol_api.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in
+           ("sol_pool_route.hip", "sol_sweep.hip", "sol_f32.hip", "sol_api.hip")]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -36,38 +36,55 @@ int check_tensors(const void* q, const void* k, const void* v, const void* out, 
     return SOL_OK;
 }
 
+// Workspace layout (each region 256-byte aligned):
+//   qbar, kbar, vsum : fp32 [H][N][d]     pooled tensors
+//   tau              : fp32 [H][N]        thresholds
+//   queues           : int32[8]           sweep work counters
+//   kbar_bf, vsum_bf : bf16 [H][N][d]     MFMA operands of the approximate path
 struct Workspace {
     float* qbar;
     float* kbar;
     float* vsum;
     float* tau;
     int* queues;
+    uint16_t* kbar_bf;
+    uint16_t* vsum_bf;
     size_t bytes;
 };
 
 Workspace carve(void* base, int H, int L, int d, int B) {
     const size_t N = ((size_t)L + B - 1) / B;
     const size_t pooled = align_up(sizeof(float) * (size_t)H * N * d);
+    const size_t pooled_bf = align_up(sizeof(uint16_t) * (size_t)H * N * d);
     const size_t taub = align_up(sizeof(float) * (size_t)H * N);
     const size_t qb = align_up(sizeof(int) * 8);
     char* p = static_cast<char*>(base);
     Workspace w;
-    w.qbar = reinterpret_cast<float*>(p);
-    w.kbar = reinterpret_cast<float*>(p + pooled);
-    w.vsum = reinterpret_cast<float*>(p + 2 * pooled);
-    w.tau = reinterpret_cast<float*>(p + 3 * pooled);
-    w.queues = reinterpret_cast<int*>(p + 3 * pooled + taub);
-    w.bytes = 3 * pooled + taub + qb;
+    size_t off = 0;
+    w.qbar = reinterpret_cast<float*>(p + off); off += pooled;
+    w.kbar = reinterpret_cast<float*>(p + off); off += pooled;
+    w.vsum = reinterpret_cast<float*>(p + off); off += pooled;
+    w.tau = reinterpret_cast<float*>(p + off); off += taub;
+    w.queues = reinterpret_cast<int*>(p + off); off += qb;
+    w.kbar_bf = reinterpret_cast<uint16_t*>(p + off); off += pooled_bf;
+    w.vsum_bf = reinterpret_cast<uint16_t*>(p + off); off += pooled_bf;
+    w.bytes = off;
     return w;
 }
 
+hipError_t launch_sweep(const sol::AttnArgs& a, int bf16, int d, int B, bool dense, hipStream_t s) {
+    return bf16 ? sol::launch_sweep_bf16(a, d, B, dense, s) : sol::launch_attn_f32(a, d, B, dense, s);
+}
+
 sol::AttnArgs sweep_args(const void* q, const void* k, const void* v, const float* qbar,
-                         const float* kbar, const float* vsum, const float* tau, int H, int L, int d,
+                         const float* kbar, const float* vsum, const float* tau,
+                         const uint16_t* kbar_bf, const uint16_t* vsum_bf, int H, int L, int d,
                          int B, void* out, int* counters, uint32_t* sel_mask) {
     const int N = (L + B - 1) / B;
     sol::AttnArgs a = {};
     a.q = q; a.k = k; a.v = v;
     a.qbar = qbar; a.kbar = kbar; a.vsum = vsum; a.tau = tau;
+    a.kbar_bf = kbar_bf; a.vsum_bf = vsum_bf;
     a.out = out;
     a.sel_dbg = sel_mask;
     a.queues = counters;
@@ -98,13 +115,14 @@ int forward(const void* q, const void* k, const void* v, int H, int L, int d, in
     // The thresholds go straight to the caller's array when it asks for them.
     float* tau = tau_out ? tau_out : w.tau;
 
-    if (sol::launch_pool(q, k, v, bf16, H, L, d, B, w.qbar, w.kbar, w.vsum, s) != hipSuccess)
+    if (sol::launch_pool(q, k, v, bf16, H, L, d, B, w.qbar, w.kbar, w.vsum,
+                         bf16 ? w.kbar_bf : nullptr, bf16 ? w.vsum_bf : nullptr, s) != hipSuccess)
         return SOL_EHIP;
     if (sol::launch_route(w.qbar, w.kbar, H, N, d, c, beta, tau, kept, w.queues, s) != hipSuccess)
         return SOL_EHIP;
-    const sol::AttnArgs a = sweep_args(q, k, v, w.qbar, w.kbar, w.vsum, tau, H, L, d, B, out,
-                                       w.queues, sel_mask);
-    if (sol::launch_attn(a, bf16, d, B, false, s) != hipSuccess) return SOL_EHIP;
+    const sol::AttnArgs a = sweep_args(q, k, v, w.qbar, w.kbar, w.vsum, tau, w.kbar_bf, w.vsum_bf,
+                                       H, L, d, B, out, w.queues, sel_mask);
+    if (launch_sweep(a, bf16, d, B, false, s) != hipSuccess) return SOL_EHIP;
     return SOL_OK;
 }
 
@@ -126,7 +144,7 @@ int sol_pool(const void* q, const void* k, const void* v, int H, int L, int d, i
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(qbar, 4) ||
         !aligned(kbar, 4) || !aligned(vsum, 4))
         return SOL_EINVAL;
-    if (sol::launch_pool(q, k, v, dt == SOL_BF16, H, L, d, B, qbar, kbar, vsum,
+    if (sol::launch_pool(q, k, v, dt == SOL_BF16, H, L, d, B, qbar, kbar, vsum, nullptr, nullptr,
                          static_cast<hipStream_t>(stream)) != hipSuccess)
         return SOL_EHIP;
     return SOL_OK;
@@ -149,20 +167,32 @@ int sol_route(const float* qbar, const float* kbar, int H, int L, int d, int B, 
 
 int sol_sweep(const void* q, const void* k, const void* v, const float* qbar, const float* kbar,
               const float* vsum, const float* tau, int H, int L, int d, int B, sol_dtype_t dt,
-              void* out, int32_t* counters, uint32_t* sel_mask, void* stream) {
+              void* out, void* workspace, size_t ws_bytes, uint32_t* sel_mask, void* stream) {
     int st = check_shape(H, L, d, B);
     if (st != SOL_OK) return st;
     st = check_tensors(q, k, v, out, dt);
     if (st != SOL_OK) return st;
-    if (!qbar || !kbar || !vsum || !tau || !counters) return SOL_EINVAL;
+    if (!qbar || !kbar || !vsum || !tau) return SOL_EINVAL;
     if (!aligned(qbar, 16) || !aligned(kbar, 16) || !aligned(vsum, 16) || !aligned(tau, 4) ||
-        !aligned(counters, 4) || (sel_mask && !aligned(sel_mask, 4)))
+        (sel_mask && !aligned(sel_mask, 4)))
         return SOL_EINVAL;
+    if (!workspace || !aligned(workspace, kAlign)) return SOL_EWORKSPACE;
+    const Workspace w = carve(workspace, H, L, d, B);
+    if (ws_bytes < w.bytes) return SOL_EWORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (sol::launch_reset_counters(counters, s) != hipSuccess) return SOL_EHIP;
-    const sol::AttnArgs a = sweep_args(q, k, v, qbar, kbar, vsum, tau, H, L, d, B, out, counters,
-                                       sel_mask);
-    if (sol::launch_attn(a, dt == SOL_BF16, d, B, false, s) != hipSuccess) return SOL_EHIP;
+    const int N = (L + B - 1) / B;
+    const int bf16 = dt == SOL_BF16;
+    // bf16 operands of the approximate path (and cleared work counters)
+    if (bf16) {
+        if (sol::launch_pooled_to_bf16(kbar, vsum, (size_t)H * N * d, w.kbar_bf, w.vsum_bf,
+                                       w.queues, s) != hipSuccess)
+            return SOL_EHIP;
+    } else if (sol::launch_reset_counters(w.queues, s) != hipSuccess) {
+        return SOL_EHIP;
+    }
+    const sol::AttnArgs a = sweep_args(q, k, v, qbar, kbar, vsum, tau, w.kbar_bf, w.vsum_bf, H, L,
+                                       d, B, out, w.queues, sel_mask);
+    if (launch_sweep(a, bf16, d, B, false, s) != hipSuccess) return SOL_EHIP;
     return SOL_OK;
 }
 
@@ -195,7 +225,7 @@ int sol_attn_dense(const void* q, const void* k, const void* v, int H, int L, in
     a.nlast = L - (N - 1) * B;
     a.c = static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
     a.c_log2e = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(d)));
-    if (sol::launch_attn(a, dt == SOL_BF16, d, B, true, static_cast<hipStream_t>(stream)) != hipSuccess)
+    if (launch_sweep(a, dt == SOL_BF16, d, B, true, static_cast<hipStream_t>(stream)) != hipSuccess)
         return SOL_EHIP;
     return SOL_OK;
 }

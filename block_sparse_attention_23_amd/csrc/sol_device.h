@@ -25,9 +25,30 @@ __device__ __forceinline__ u16 f32_to_bf16_bits(float f) {
     return static_cast<u16>(u >> 16);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (round to nearest even; one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return static_cast<uint32_t>(f32_to_bf16_bits(lo)) |
-           (static_cast<uint32_t>(f32_to_bf16_bits(hi)) << 16);
+    const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Reductions over the four lanes l, l^16, l^32, l^48 (one query row of a
+// 16x16 MFMA tile) with the gfx950 lane-swap instructions: after a swap of x
+// with itself the two results hold both 16-lane (or 32-lane) halves, so
+// combining them gives every lane the partner's value folded in.
+__device__ __forceinline__ float max4rows(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float sum4rows(float x) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16) on one wavefront.
@@ -85,6 +106,23 @@ __device__ __forceinline__ float proxy_from_quarter(const float* qbar_lds, const
     const float s01 = acc + __shfl_xor(acc, 1);
     const float s = s01 + __shfl_xor(s01, 2);
     return s * scale;
+}
+
+// Persistent-kernel work queues: eight counters, one per XCD (workgroup w
+// runs on XCD w % 8).  Queue x holds, head by head, the query blocks
+// [x N / 8, (x+1) N / 8).  Returns h * N + i, or -1 once all queues are empty.
+__device__ __forceinline__ int claim_item(int* queues, int H, int N) {
+    const int xcd = blockIdx.x & 7;
+#pragma unroll 1
+    for (int t = 0; t < 8; ++t) {
+        const int x = (xcd + t) & 7;
+        const int lo = (x * N) >> 3, hi = ((x + 1) * N) >> 3;
+        const int nx = hi - lo;
+        if (nx == 0) continue;
+        const int kk = atomicAdd(&queues[x], 1);
+        if (kk < H * nx) return (kk / nx) * N + lo + (kk % nx);
+    }
+    return -1;
 }
 
 }  // namespace sol

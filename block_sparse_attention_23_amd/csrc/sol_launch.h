@@ -14,6 +14,8 @@ struct AttnArgs {
     const float* kbar;
     const float* vsum;
     const float* tau;    // [H][N] fp32 (unused by dense)
+    const uint16_t* kbar_bf;  // [H][N][d] bf16 copy of kbar (bf16 sweep, approximate path)
+    const uint16_t* vsum_bf;  // [H][N][d] bf16 copy of vsum
     void* out;
     uint32_t* sel_dbg;   // [H][N][W] or null
     int* queues;         // 8 per-XCD work counters (sol only)
@@ -25,10 +27,14 @@ struct AttnArgs {
 
 // Each returns hipSuccess or the launch error.
 hipError_t launch_pool(const void* q, const void* k, const void* v, int bf16, int H, int L,
-                       int d, int B, float* qbar, float* kbar, float* vsum, hipStream_t s);
+                       int d, int B, float* qbar, float* kbar, float* vsum, uint16_t* kbar_bf,
+                       uint16_t* vsum_bf, hipStream_t s);
+hipError_t launch_pooled_to_bf16(const float* kbar, const float* vsum, size_t n, uint16_t* kbar_bf,
+                                 uint16_t* vsum_bf, int* queues, hipStream_t s);
 hipError_t launch_route(const float* qbar, const float* kbar, int H, int N, int d, float c,
                         float beta, float* tau, int32_t* kept, int* queues, hipStream_t s);
+hipError_t launch_sweep_bf16(const AttnArgs& a, int d, int B, bool dense, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, int d, int B, bool dense, hipStream_t s);
 hipError_t launch_reset_counters(int* queues, hipStream_t s);
-hipError_t launch_attn(const AttnArgs& a, int bf16, int d, int B, bool dense, hipStream_t s);
 
 }  // namespace sol

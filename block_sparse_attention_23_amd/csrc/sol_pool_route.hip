@@ -1,0 +1,276 @@
+// sol_pool_route.hip -- the two stages before the sweep ("Sol-Attn" visual
+// explainer, "The complete idea in one pass": pool Q, K and V into blocks;
+// the threshold-computation stage before the proxy-score stream).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "sol_device.h"
+#include "sol_launch.h"
+
+namespace sol {
+
+// ============================================================================
+// pool: block means of Q and K, block sums of V (Eq. (5) and Eq. (10)
+// legends).  One workgroup per (head, block), one pass over the block's
+// tokens.  Thread t reads 16-byte vectors at column chunk t % CH of rows
+// t / CH, t / CH + RG, ...; the RG row-group partial sums are added in a
+// fixed order through LDS.  Optionally also writes bf16 copies of kbar and
+// vsum, which the sweep's approximate path feeds to the MFMA.
+// ============================================================================
+template <typename T, int D, int BLK>
+__global__ void __launch_bounds__(256) pool_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                                                   const T* __restrict__ v, int L, int N,
+                                                   float* __restrict__ qbar,
+                                                   float* __restrict__ kbar,
+                                                   float* __restrict__ vsum,
+                                                   u16* __restrict__ kbar_bf,
+                                                   u16* __restrict__ vsum_bf) {
+    constexpr int VEC = 16 / sizeof(T);
+    constexpr int CH = D / VEC;
+    constexpr int RG = 256 / CH;
+    constexpr int IT = (BLK + RG - 1) / RG;
+    __shared__ float red[3][RG][D + 1];
+
+    const int item = blockIdx.x;  // h * N + j
+    const int h = item / N, j = item % N;
+    const int t0 = j * BLK;
+    const int n = min(BLK, L - t0);
+    const int tid = threadIdx.x;
+    const int ch = tid % CH, rg = tid / CH;
+
+    float aq[VEC], ak[VEC], av[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) aq[e] = ak[e] = av[e] = 0.0f;
+
+    const size_t base = ((size_t)h * L + t0) * D + ch * VEC;
+#pragma unroll
+    for (int it0 = 0; it0 < IT; it0 += 4) {
+        u32x4_t bq[4], bk[4], bv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int r = rg + (it0 + u) * RG;
+            if (it0 + u < IT && r < n) {
+                bq[u] = *reinterpret_cast<const u32x4_t*>(q + base + (size_t)r * D);
+                bk[u] = *reinterpret_cast<const u32x4_t*>(k + base + (size_t)r * D);
+                bv[u] = *reinterpret_cast<const u32x4_t*>(v + base + (size_t)r * D);
+            } else {
+                bq[u] = bk[u] = bv[u] = u32x4_t{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                float xq, xk, xv;
+                if constexpr (sizeof(T) == 2) {
+                    const int sh = (e & 1) ? 16 : 0;
+                    xq = bf16_bits_to_f32(static_cast<u16>(bq[u][e / 2] >> sh));
+                    xk = bf16_bits_to_f32(static_cast<u16>(bk[u][e / 2] >> sh));
+                    xv = bf16_bits_to_f32(static_cast<u16>(bv[u][e / 2] >> sh));
+                } else {
+                    xq = __uint_as_float(bq[u][e]);
+                    xk = __uint_as_float(bk[u][e]);
+                    xv = __uint_as_float(bv[u][e]);
+                }
+                aq[e] += xq;
+                ak[e] += xk;
+                av[e] += xv;
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+        red[0][rg][ch * VEC + e] = aq[e];
+        red[1][rg][ch * VEC + e] = ak[e];
+        red[2][rg][ch * VEC + e] = av[e];
+    }
+    __syncthreads();
+    const float inv_n = 1.0f / static_cast<float>(n);
+    for (int x = tid; x < 3 * D; x += 256) {
+        const int which = x / D, col = x % D;
+        float s = 0.0f;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) s += red[which][r][col];
+        const size_t o = (size_t)item * D + col;
+        if (which == 0) {
+            qbar[o] = s * inv_n;
+        } else if (which == 1) {
+            const float m = s * inv_n;
+            kbar[o] = m;
+            if (kbar_bf) kbar_bf[o] = f32_to_bf16_bits(m);
+        } else {
+            vsum[o] = s;
+            if (vsum_bf) vsum_bf[o] = f32_to_bf16_bits(s);
+        }
+    }
+}
+
+__global__ void reset_counters_kernel(int* queues) {
+    if (threadIdx.x < 8) queues[threadIdx.x] = 0;
+}
+
+// bf16 copies of kbar and vsum for sol_sweep callers that bring their own
+// pooled tensors; workgroup 0 also clears the sweep's work counters.
+__global__ void __launch_bounds__(256) pooled_to_bf16_kernel(const float* __restrict__ kbar,
+                                                             const float* __restrict__ vsum,
+                                                             size_t n, u16* __restrict__ kbar_bf,
+                                                             u16* __restrict__ vsum_bf,
+                                                             int* __restrict__ queues) {
+    if (blockIdx.x == 0 && threadIdx.x < 8) queues[threadIdx.x] = 0;
+    for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < n; x += (size_t)gridDim.x * 256) {
+        kbar_bf[x] = f32_to_bf16_bits(kbar[x]);
+        vsum_bf[x] = f32_to_bf16_bits(vsum[x]);
+    }
+}
+
+// ============================================================================
+// route: per (head h, query block i) the proxy row s_i. over all N key
+// blocks (Eq. (11) right-hand side), its population mean and standard
+// deviation (Eq. (5)), tau_i = mu_i + beta sigma_i and the kept count
+// |{j : s_ij > tau_i}| (Eq. (4)).  One workgroup (256 threads) serves R
+// consecutive query blocks of one head, so each pooled key is read once per
+// R rows; the rows live in dynamic LDS only.  Each s_ij is computed with the
+// shared four-lane routine, exactly as the sweep recomputes it.
+// ============================================================================
+template <int D, int R>
+__global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qbar,
+                                                    const float* __restrict__ kbar, int N,
+                                                    int groups_per_head, float c, float beta,
+                                                    float* __restrict__ tau_out,
+                                                    int32_t* __restrict__ kept,
+                                                    int* __restrict__ queues) {
+    extern __shared__ float rows[];  // [R][N]
+    __shared__ float qb[R][D];
+    const int h = blockIdx.x / groups_per_head;
+    const int i0 = (blockIdx.x % groups_per_head) * R;
+    const int nr = min(R, N - i0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (queues && blockIdx.x == 0 && tid < 8) queues[tid] = 0;
+    for (int t = tid; t < R * D; t += 256) {
+        const int r = t / D, x = t % D;
+        qb[r][x] = r < nr ? qbar[((size_t)h * N + i0 + r) * D + x] : 0.0f;
+    }
+    __syncthreads();
+
+    const int jj = tid >> 2, qq = tid & 3;
+    for (int j0 = 0; j0 < N; j0 += 64) {
+        const int j = j0 + jj;
+        float kv[D / 4];
+        load_kbar_quarter<D>(kbar + ((size_t)h * N + min(j, N - 1)) * D, qq, kv);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float s = proxy_from_quarter<D>(qb[r], kv, qq, c);
+            if (qq == 0 && j < N) rows[r * N + j] = s;
+        }
+    }
+    __syncthreads();
+
+    // statistics: wave w handles rows w, w+4, ... (lane-strided sums in a
+    // fixed order, then a butterfly whose result every lane shares)
+    for (int r = wave; r < nr; r += 4) {
+        const float* row = rows + r * N;
+        float part = 0.0f;
+        for (int j = lane; j < N; j += 64) part += row[j];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
+        const float mu = part / static_cast<float>(N);
+        float pv = 0.0f;
+        for (int j = lane; j < N; j += 64) {
+            const float dlt = row[j] - mu;
+            pv = __builtin_fmaf(dlt, dlt, pv);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) pv += __shfl_xor(pv, off);
+        const float sigma = sqrtf(fmaxf(pv / static_cast<float>(N), 0.0f));
+        float tau;
+        if (isinf(beta)) tau = beta;  // -inf: every block exact; +inf: none
+        else tau = __builtin_fmaf(beta, sigma, mu);
+        int cnt = 0;
+        for (int j = lane; j < N; j += 64) cnt += row[j] > tau ? 1 : 0;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
+        if (lane == 0) {
+            tau_out[(size_t)h * N + i0 + r] = tau;
+            kept[(size_t)h * N + i0 + r] = cnt;
+        }
+    }
+}
+
+// ============================================================================
+// launchers
+// ============================================================================
+namespace {
+
+template <int D, int BLK>
+hipError_t pool_t(const void* q, const void* k, const void* v, int bf16, int H, int L, int N,
+                  float* qbar, float* kbar, float* vsum, u16* kbar_bf, u16* vsum_bf, hipStream_t s) {
+    dim3 grid(H * N), block(256);
+    if (bf16)
+        hipLaunchKernelGGL((pool_kernel<u16, D, BLK>), grid, block, 0, s, static_cast<const u16*>(q),
+                           static_cast<const u16*>(k), static_cast<const u16*>(v), L, N, qbar, kbar,
+                           vsum, kbar_bf, vsum_bf);
+    else
+        hipLaunchKernelGGL((pool_kernel<float, D, BLK>), grid, block, 0, s,
+                           static_cast<const float*>(q), static_cast<const float*>(k),
+                           static_cast<const float*>(v), L, N, qbar, kbar, vsum, kbar_bf, vsum_bf);
+    return hipGetLastError();
+}
+
+template <int D, int R>
+hipError_t route_t(const float* qbar, const float* kbar, int H, int N, float c, float beta,
+                   float* tau, int32_t* kept, int* queues, hipStream_t s) {
+    const int gph = (N + R - 1) / R;
+    const size_t shm = sizeof(float) * (size_t)R * N;
+    hipLaunchKernelGGL((route_kernel<D, R>), dim3(H * gph), dim3(256), shm, s, qbar, kbar, N, gph, c,
+                       beta, tau, kept, queues);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t route_d(const float* qbar, const float* kbar, int H, int N, float c, float beta,
+                   float* tau, int32_t* kept, int* queues, hipStream_t s) {
+    // as many rows per workgroup as 64 KB of LDS holds
+    const size_t row_bytes = sizeof(float) * ((size_t)N + D);
+    if (16 * row_bytes <= 65536) return route_t<D, 16>(qbar, kbar, H, N, c, beta, tau, kept, queues, s);
+    if (8 * row_bytes <= 65536) return route_t<D, 8>(qbar, kbar, H, N, c, beta, tau, kept, queues, s);
+    if (4 * row_bytes <= 65536) return route_t<D, 4>(qbar, kbar, H, N, c, beta, tau, kept, queues, s);
+    if (2 * row_bytes <= 65536) return route_t<D, 2>(qbar, kbar, H, N, c, beta, tau, kept, queues, s);
+    return route_t<D, 1>(qbar, kbar, H, N, c, beta, tau, kept, queues, s);
+}
+
+}  // namespace
+
+hipError_t launch_pool(const void* q, const void* k, const void* v, int bf16, int H, int L, int d,
+                       int B, float* qbar, float* kbar, float* vsum, u16* kbar_bf, u16* vsum_bf,
+                       hipStream_t s) {
+    const int N = (L + B - 1) / B;
+    if (d == 64 && B == 64) return pool_t<64, 64>(q, k, v, bf16, H, L, N, qbar, kbar, vsum, kbar_bf, vsum_bf, s);
+    if (d == 64 && B == 128) return pool_t<64, 128>(q, k, v, bf16, H, L, N, qbar, kbar, vsum, kbar_bf, vsum_bf, s);
+    if (d == 128 && B == 64) return pool_t<128, 64>(q, k, v, bf16, H, L, N, qbar, kbar, vsum, kbar_bf, vsum_bf, s);
+    if (d == 128 && B == 128) return pool_t<128, 128>(q, k, v, bf16, H, L, N, qbar, kbar, vsum, kbar_bf, vsum_bf, s);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_pooled_to_bf16(const float* kbar, const float* vsum, size_t n, u16* kbar_bf,
+                                 u16* vsum_bf, int* queues, hipStream_t s) {
+    const size_t blocks = (n + 255) / 256;
+    const int grid = static_cast<int>(blocks < 4096 ? (blocks ? blocks : 1) : 4096);
+    hipLaunchKernelGGL(pooled_to_bf16_kernel, dim3(grid), dim3(256), 0, s, kbar, vsum, n, kbar_bf,
+                       vsum_bf, queues);
+    return hipGetLastError();
+}
+
+hipError_t launch_reset_counters(int* queues, hipStream_t s) {
+    hipLaunchKernelGGL(reset_counters_kernel, dim3(1), dim3(64), 0, s, queues);
+    return hipGetLastError();
+}
+
+hipError_t launch_route(const float* qbar, const float* kbar, int H, int N, int d, float c,
+                        float beta, float* tau, int32_t* kept, int* queues, hipStream_t s) {
+    if (d == 64) return route_d<64>(qbar, kbar, H, N, c, beta, tau, kept, queues, s);
+    if (d == 128) return route_d<128>(qbar, kbar, H, N, c, beta, tau, kept, queues, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace sol

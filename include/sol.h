@@ -49,7 +49,8 @@ typedef enum {
 /*
  * Bytes of device workspace sol_attn_fwd / sol_attn_fwd_dbg need for this
  * shape: the pooled tensors (3 x H*N*d fp32), the per-query-block thresholds
- * (H*N fp32) and the scheduler's queue counters.  0 for invalid shapes.
+ * (H*N fp32), the scheduler's queue counters and bf16 copies of the pooled
+ * keys and summed values (2 x H*N*d bf16).  0 for invalid shapes.
  */
 size_t sol_workspace_bytes(int H, int L, int d, int B);
 
@@ -87,13 +88,17 @@ int sol_route(const float* qbar, const float* kbar, int H, int L, int d, int B,
  * route each key block (s_ij > tau_i: exact; otherwise approximate) and merge
  * both paths into one online softmax ("Sol-Attn" visual explainer, Eq. (9),
  * Eq. (10), Eq. (11); abstract).  Output as sol_attn_fwd.
- * counters : DEVICE int32[8] scratch for the work queues (overwritten).
- * sel_mask : as in sol_attn_fwd_dbg, or NULL.
+ * qbar, kbar, vsum : DEVICE fp32 [H][N][d] as written by sol_pool.
+ * tau       : DEVICE fp32 [H][N] as written by sol_route.
+ * workspace : DEVICE, at least sol_workspace_bytes(H, L, d, B) bytes,
+ *             256-byte aligned (scratch: work counters and bf16 copies of the
+ *             pooled keys and summed values).
+ * sel_mask  : as in sol_attn_fwd_dbg, or NULL.
  */
 int sol_sweep(const void* q, const void* k, const void* v,
               const float* qbar, const float* kbar, const float* vsum, const float* tau,
               int H, int L, int d, int B, sol_dtype_t dt, void* out,
-              int32_t* counters, uint32_t* sel_mask, void* stream);
+              void* workspace, size_t ws_bytes, uint32_t* sel_mask, void* stream);
 
 /*
  * Sol-Attn forward ("Sol-Attn" visual explainer: Eq. (4) selection rule,

@@ -97,10 +97,13 @@ def test_stage_entry_points_reject_bad_arguments(lib):
     assert lib.sol_route(FAKE, None, 1, 100, 64, 64, 1.0, FAKE, FAKE, None) == -1
     assert lib.sol_route(FAKE, FAKE, 1, 100, 64, 64, math.nan, FAKE, FAKE, None) == -1
     assert lib.sol_route(FAKE, FAKE, 1, 100, 64, 16, 1.0, FAKE, FAKE, None) == -2
-    args = [FAKE] * 7 + [1, 100, 64, 64, 0, FAKE, FAKE, None, None]
+    args = [FAKE] * 7 + [1, 100, 64, 64, 0, FAKE, FAKE_WS, 1 << 30, None, None]
     bad = list(args)
-    bad[13] = None  # counters
-    assert lib.sol_sweep(*bad) == -1
+    bad[13] = None  # workspace
+    assert lib.sol_sweep(*bad) == -3
+    bad = list(args)
+    bad[14] = 64  # workspace too small
+    assert lib.sol_sweep(*bad) == -3
     bad = list(args)
     bad[6] = None  # tau
     assert lib.sol_sweep(*bad) == -1
