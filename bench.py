@@ -111,8 +111,9 @@ def cpu_baseline(w, inp_head0, beta, target_s):
         oracle.merge(q, k, v, kbar, vsum, B, r["sel"], rows=rows)
         return time.perf_counter() - t
 
-    t1 = merge_blocks(2) / 2
-    n = max(2, min(w.N, int(max(1.0, target_s - t_prep) / max(t1, 1e-6))))
+    merge_blocks(1)  # warm the thread pool and caches
+    t1 = merge_blocks(8) / 8
+    n = max(8, min(w.N, int(max(1.0, target_s - t_prep) / max(t1, 1e-6))))
     t_merge = merge_blocks(n)
     total = t_prep + t_merge
     flops = n * B * 4.0 * L * d
