@@ -1,38 +1,39 @@
 // sol_sweep.hip -- the fused Sol-Attn sweep for bf16 inputs on gfx950.
 //
-// One workgroup owns one query block of BLK rows at a time; wave w owns the
-// 32 rows 32w .. 32w+31 (two 16-row MFMA tiles), so each K / V fragment read
-// from LDS feeds two v_mfma_f32_16x16x32_bf16.
+// A workgroup (4 waves) owns 128 query rows at a time: two 64-row query
+// blocks (B = 64) or one 128-row block (B = 128).  Wave w owns rows
+// 32w .. 32w+31 as two 16-row tiles of v_mfma_f32_16x16x32_bf16.
 //
-// Per query block i of head h ("Sol-Attn" visual explainer, "The complete
-// idea in one pass", Eq. (4), Eq. (9), Eq. (10), Eq. (11)):
-//   1. routing, on chip: the proxy scores s_ij of all N pooled keys are
-//      recomputed chunk by chunk with the routing kernel's own arithmetic and
-//      compared with tau_i; the decisions become an N-bit mask in LDS and a
-//      tile list: one approximate tile per chunk of BLK pooled keys that has
-//      an unselected block, then one exact tile per selected key block.
-//      Scores are never written to memory.
-//   2. the tile loop: every tile is BLK keys (pooled keys, or the tokens of a
-//      key block) and BLK values (summed values, or the tokens' values),
-//      staged in LDS as K [key][d] and V^T [d][key].  Scores are formed
-//      transposed, S^T = K Q^T, so each lane holds one query row per 16-row
-//      tile and 4 keys per 16-key tile, and the softmax weights feed
-//      O^T += V^T P^T from registers.  Approximate tiles weight each pooled
-//      key by n_j tokens in the denominator (Eq. (9)) and use summed values
-//      (Eq. (10)); selected columns of an approximate tile and padded keys of
-//      the last block are masked.  One running max / denominator /
-//      accumulator serves both paths.
+// Per workgroup ("Sol-Attn" visual explainer, "The complete idea in one
+// pass", Eq. (4), Eq. (9), Eq. (10), Eq. (11)):
+//   1. routing on chip: the proxy scores s_ij of every pooled key are
+//      recomputed with the routing kernel's own arithmetic and compared with
+//      tau_i of each query block, giving one N-bit decision mask per block in
+//      LDS.  Scores are never written to memory.  A tile list follows: one
+//      approximate entry per chunk of B pooled keys that holds an unselected
+//      block of either query block, then one exact entry per key block that
+//      either query block selected (the union, so a key block chosen by both
+//      is loaded once), each tagged with the query blocks that use it.
+//   2. the tile loop over 64-key tiles.  Tiles stream from HBM straight into
+//      LDS (global_load_lds, 16 bytes a lane) into two buffers, so the next
+//      tile loads while the current one is computed; K and V stay row-major
+//      in LDS with an XOR swizzle of 16-byte chunks.  Scores are formed
+//      transposed, S^T = K Q^T (each lane: one query row per 16-row tile, 4
+//      keys per 16-key tile), and O^T += V^T P^T takes V^T through the
+//      transposing LDS read (ds_read_b64_tr_b16) and P^T from registers.
+//      Approximate tiles weight each pooled key by the n_j tokens it stands
+//      for in the denominator (Eq. (9)) and use summed values (Eq. (10));
+//      their selected columns, and padded keys of a ragged last block, are
+//      masked.  One running max / denominator / accumulator serves both.
 //   3. out = O / l, rounded to bf16.
-// Tiles are software-pipelined: the global loads of tile t+1 are in flight
-// in registers while tile t is computed from LDS.
 //
-// Scheduling: persistent workgroups pull query blocks from eight work
+// Scheduling: persistent workgroups pull 128-row groups from eight work
 // queues, one per XCD (workgroup w runs on XCD w % 8).  Queue x holds, head
-// by head, the query blocks [x N / 8, (x+1) N / 8), so the workgroups of one
-// XCD work on neighbouring query blocks of the same head at the same time
-// and share its L2; an empty queue sends a workgroup on to the next one.
-// Every workgroup exits once all eight queues are drained.  Dense mode:
-// every key block exact, no routing, one query block per workgroup.
+// by head, the groups [x G / 8, (x+1) G / 8) of the head's G groups, so the
+// workgroups of one XCD work on neighbouring rows of the same head at the
+// same time and share its L2.  Every workgroup exits once all eight queues
+// are drained.  Dense mode: every key block exact, no routing, one group per
+// workgroup.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -42,30 +43,32 @@
 
 namespace sol {
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
 template <int D, int BLK>
 struct Sweep {
-    static constexpr int NW = BLK / 32;              // waves, 32 query rows each
-    static constexpr int NT = 64 * NW;               // threads
-    static constexpr int KP = D + 8;                 // K tile pitch (bf16 elements)
-    static constexpr int VP = BLK;                   // V^T tile pitch (XOR-swizzled, no padding)
-    static constexpr int NKT = BLK / 16;             // 16-key tiles of S^T
-    static constexpr int NS = D / 32;                // 32-deep steps over d
-    static constexpr int NDT = D / 16;               // 16-wide d tiles of O^T
-    static constexpr int NU = BLK / 32;              // 32-key steps of P V
-    static constexpr int KPT = (BLK * D / 8) / NT;   // 16-byte K chunks per thread (D/16)
-    static constexpr int VPT = ((BLK / 4) * (D / 8)) / NT;  // (4 keys x 8 d) V units per thread
-    static_assert(KPT * NT == BLK * D / 8, "K staging must divide evenly");
-    static_assert(VPT * NT == (BLK / 4) * (D / 8), "V staging must divide evenly");
-    static constexpr int KEYS_PER_PASS = NT / 4;     // routing: four lanes per pooled key
+    static constexpr int NT = 256;                      // 4 waves
+    static constexpr int QB = 128 / BLK;                // query blocks per workgroup
+    static constexpr int SUB = BLK / 64;                // 64-key tiles per key block
+    static constexpr int CH = D / 8;                    // 16-byte chunks per row
+    static constexpr int RPK = 1024 / (2 * D);          // rows per 1 KB of LDS
+    static constexpr int LPT = (64 * D * 2) / (NT * 16);  // direct loads per thread per tile
+    static constexpr int NS = D / 32;                   // 32-deep steps over d
+    static constexpr int NDT = D / 16;                  // 16-wide d tiles of O^T
+    static constexpr int TILE = 64 * D;                 // elements of a K (or V) tile
 };
 
-constexpr uint32_t kApprox = 0x80000000u;  // tile-list flag: approximate chunk
+constexpr uint32_t kApprox = 0x80000000u;  // tile-list entry: approximate chunk
+constexpr int kPartShift = 29;             // bits 29..30: query blocks using the entry
+constexpr uint32_t kIndexMask = (1u << kPartShift) - 1u;
 
-// V^T tiles keep 4-key (8-byte) groups; group k of row d is stored at
-// position k ^ vt_swz(d).  With a pitch of BLK keys this makes both the
-// transposing stores (16 lanes on 16 rows d = 8 dc + e) and the P V operand
-// reads (16 lanes on 16 consecutive rows) hit 32 distinct LDS banks.
-__device__ __forceinline__ int vt_swz(int d) { return (d & 15) ^ ((d >> 3) & 15); }
+// K tiles: 16-byte chunk c of row r sits at position c ^ (r & 7); V tiles at
+// c ^ 2 (r & 3).  Both make the MFMA operand reads (b128 rows for K, the
+// transposing b64 read for V) hit 32 distinct banks.
+__device__ __forceinline__ int k_swz(int r) { return r & 7; }
+__device__ __forceinline__ int v_swz(int r) { return (r & 3) << 1; }
 
 // Keep bits 0, 4, 8, ..., 60 of m and pack them into bits 0..15.
 __device__ __forceinline__ uint32_t every_fourth_bit(uint64_t m) {
@@ -77,72 +80,41 @@ __device__ __forceinline__ uint32_t every_fourth_bit(uint64_t m) {
     return static_cast<uint32_t>(x);
 }
 
+// Issue the direct-to-LDS loads of one 64-row tile: rows row0 .. row0+63 of
+// the K-like and V-like sources (row stride D, rows past rowmax repeat
+// rowmax -- their columns are masked).  Wave w fills 1 KB blocks w*LPT ..
+// w*LPT+LPT-1; lane l writes the 16 bytes at block + 16 l.
 template <int D, int BLK>
-struct TileRegs {
-    u32x4_t k[Sweep<D, BLK>::KPT];
-    u32x4_t v[Sweep<D, BLK>::VPT][4];
-};
-
-// Issue the global loads of one tile (BLK rows of K-like and V-like data,
-// row-major bf16 with row stride D); rows at or past `nvalid` read as 0.
-template <int D, int BLK>
-__device__ __forceinline__ void tile_load(TileRegs<D, BLK>& tr, const u16* __restrict__ kp,
-                                          const u16* __restrict__ vp, int nvalid, int tid) {
+__device__ __forceinline__ void tile_issue(const u16* __restrict__ kp, const u16* __restrict__ vp,
+                                           int row0, int rowmax, u16* Kdst, u16* Vdst, int wave,
+                                           int lane) {
     using S = Sweep<D, BLK>;
 #pragma unroll
-    for (int it = 0; it < S::KPT; ++it) {
-        const int c = tid + it * S::NT;
-        const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-        tr.k[it] = r < nvalid ? *reinterpret_cast<const u32x4_t*>(kp + (size_t)r * D + col)
-                              : u32x4_t{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int it = 0; it < S::VPT; ++it) {
-        const int u = tid + it * S::NT;
-        const int kg = u / (D / 8), dc = u % (D / 8);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int r = kg * 4 + rr;
-            tr.v[it][rr] = r < nvalid ? *reinterpret_cast<const u32x4_t*>(vp + (size_t)r * D + dc * 8)
-                                      : u32x4_t{0u, 0u, 0u, 0u};
-        }
-    }
-}
-
-// Write a loaded tile to LDS: K row-major, V transposed (4 keys per 8-byte write).
-template <int D, int BLK>
-__device__ __forceinline__ void tile_store(const TileRegs<D, BLK>& tr, u16* Ks, u16* Vt, int tid) {
-    using S = Sweep<D, BLK>;
-#pragma unroll
-    for (int it = 0; it < S::KPT; ++it) {
-        const int c = tid + it * S::NT;
-        const int r = c / (D / 8), col = (c % (D / 8)) * 8;
-        *reinterpret_cast<u32x4_t*>(Ks + r * S::KP + col) = tr.k[it];
-    }
-#pragma unroll
-    for (int it = 0; it < S::VPT; ++it) {
-        const int u = tid + it * S::NT;
-        const int kg = u / (D / 8), dc = u % (D / 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            // element e of four key rows -> {k0 | k1 << 16, k2 | k3 << 16}
-            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            const u32x2_t w2 = {__builtin_amdgcn_perm(tr.v[it][1][e / 2], tr.v[it][0][e / 2], sel),
-                                __builtin_amdgcn_perm(tr.v[it][3][e / 2], tr.v[it][2][e / 2], sel)};
-            const int d = dc * 8 + e;
-            *reinterpret_cast<u32x2_t*>(Vt + d * S::VP + ((kg ^ vt_swz(d)) << 2)) = w2;
-        }
+    for (int i = 0; i < S::LPT; ++i) {
+        const int bi = wave * S::LPT + i;
+        const int r = bi * S::RPK + lane / S::CH;
+        const int ph = lane % S::CH;
+        const size_t srow = (size_t)min(row0 + r, rowmax) * D;
+        __builtin_amdgcn_global_load_lds(kp + srow + ((ph ^ k_swz(r)) << 3),
+                                         (lds_void_t*)(Kdst + bi * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vp + srow + ((ph ^ v_swz(r)) << 3),
+                                         (lds_void_t*)(Vdst + bi * 512), 16, 0, 0);
     }
 }
 
 template <int D, int BLK, bool DENSE>
-__global__ void __launch_bounds__(2 * BLK) sweep_bf16_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
     using S = Sweep<D, BLK>;
-    __shared__ __align__(16) u16 Ks[BLK * S::KP];
-    __shared__ __align__(16) u16 Vt[D * S::VP];
-    __shared__ __align__(16) float qb_s[D];
+    // two tile buffers as four distinct objects, so the compiler can tell
+    // that the loads landing in one buffer do not alias reads of the other
+    __shared__ __align__(16) u16 K0[S::TILE];
+    __shared__ __align__(16) u16 V0[S::TILE];
+    __shared__ __align__(16) u16 K1[S::TILE];
+    __shared__ __align__(16) u16 V1[S::TILE];
+    __shared__ __align__(16) float qb_s[S::QB][D];
+    __shared__ float tau_s[S::QB];
     __shared__ int misc_s[2];
-    extern __shared__ __align__(16) uint32_t dyn[];  // selection bits, then the tile list
+    extern __shared__ __align__(16) uint32_t dyn[];  // selection bits per block, then tile list
 
     const u16* __restrict__ qg = static_cast<const u16*>(a.q);
     const u16* __restrict__ kg = static_cast<const u16*>(a.k);
@@ -153,12 +125,14 @@ __global__ void __launch_bounds__(2 * BLK) sweep_bf16_kernel(AttnArgs a) {
     const int H = a.H, L = a.L, N = a.N;
     const int NC = (N + BLK - 1) / BLK;
     const int nwords = (N + 31) / 32;
-    uint32_t* selbits = dyn;                 // N bits (1 = exact)
-    uint32_t* tiles = dyn + nwords;          // up to NC + N entries
+    const int NG = (N + S::QB - 1) / S::QB;  // 128-row groups per head
+    uint32_t* selbits = dyn;                 // [QB][nwords]
+    uint32_t* tiles = dyn + S::QB * nwords;  // up to NC + N entries
+    const int myb = (wave * 32) / BLK;       // this wave's query block within the group
 
     int dense_item = -1;
     if (DENSE) {
-        const int total = H * N;
+        const int total = H * NG;
         const int per = (total + 7) / 8;
         const int idx = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
         if ((int)(blockIdx.x >> 3) >= per || idx >= total) return;
@@ -171,82 +145,96 @@ __global__ void __launch_bounds__(2 * BLK) sweep_bf16_kernel(AttnArgs a) {
             item = dense_item;
         } else {
             __syncthreads();
-            if (tid == 0) misc_s[0] = claim_item(a.queues, H, N);
+            if (tid == 0) misc_s[0] = claim_item(a.queues, H, NG);
             __syncthreads();
             item = misc_s[0];
             if (item < 0) break;
         }
-        const int h = item / N, i = item % N;
-        const int q0 = i * BLK;
+        const int h = item / NG, gi = item % NG;
+        const int i0 = gi * S::QB;
+        const int nqb = min(S::QB, N - i0);  // valid query blocks in this group
+        const int q0 = gi * 128;
         const size_t head_off = (size_t)h * L * D;
 
         int T;
         if (DENSE) {
             T = N;
         } else {
-            // ---- 1. routing on chip -------------------------------------
-            for (int t = tid; t < D; t += S::NT) qb_s[t] = a.qbar[(size_t)item * D + t];
-            const float tau_i = a.tau[item];
+            // ---- 1. routing on chip --------------------------------------
+            for (int t = tid; t < S::QB * D; t += S::NT) {
+                const int b = t / D, x = t % D;
+                qb_s[b][x] = b < nqb ? a.qbar[((size_t)h * N + i0 + b) * D + x] : 0.0f;
+            }
+            if (tid < S::QB) tau_s[tid] = tid < nqb ? a.tau[(size_t)h * N + i0 + tid] : INFINITY;
             __syncthreads();
             {
                 const int jj = tid >> 2, qq = tid & 3;
                 const size_t kb_head = (size_t)h * N * D;
-                for (int j0 = 0; j0 < N; j0 += S::KEYS_PER_PASS) {
+                for (int j0 = 0; j0 < N; j0 += 64) {
                     const int j = j0 + jj;
                     float kv[D / 4];
                     load_kbar_quarter<D>(a.kbar + kb_head + (size_t)min(j, N - 1) * D, qq, kv);
-                    const float s = proxy_from_quarter<D>(qb_s, kv, qq, a.c);
-                    const bool sel = j < N && s > tau_i;
-                    const uint32_t bits = every_fourth_bit(__ballot(sel));  // 16 keys of this wave
-                    const int kb = j0 + wave * 16;                          // first key of the wave
-                    if (lane == 0 && kb < N) {
-                        // 16-bit aligned field of the mask
-                        reinterpret_cast<uint16_t*>(selbits)[kb >> 4] = static_cast<uint16_t>(bits);
+#pragma unroll
+                    for (int b = 0; b < S::QB; ++b) {
+                        const float s = proxy_from_quarter<D>(qb_s[b], kv, qq, a.c);
+                        const bool sel = j < N && s > tau_s[b];
+                        const uint32_t bits = every_fourth_bit(__ballot(sel));
+                        const int kb = j0 + wave * 16;
+                        if (lane == 0 && kb < N)
+                            reinterpret_cast<uint16_t*>(selbits + b * nwords)[kb >> 4] =
+                                static_cast<uint16_t>(bits);
                     }
                 }
             }
             __syncthreads();
             if (wave == 0) {
-                // approximate chunks that hold at least one unselected block
                 int nt = 0;
+                // approximate chunks that hold an unselected block of a query block
                 for (int c0 = 0; c0 < NC; c0 += 64) {
                     const int c = c0 + lane;
-                    bool need = false;
+                    uint32_t part = 0;
                     if (c < NC) {
                         const int lo = c * BLK, cnt = min(BLK, N - lo);
-                        int ones = 0;
+                        for (int b = 0; b < nqb; ++b) {
+                            int ones = 0;
 #pragma unroll
-                        for (int w32 = 0; w32 < BLK / 32; ++w32) {
-                            const int bit0 = lo + 32 * w32;
-                            if (bit0 < N) {
-                                uint32_t wd = selbits[bit0 >> 5];
-                                const int valid = min(32, N - bit0);
-                                if (valid < 32) wd &= (1u << valid) - 1u;
-                                ones += __popc(wd);
+                            for (int w32 = 0; w32 < BLK / 32; ++w32) {
+                                const int bit0 = lo + 32 * w32;
+                                if (bit0 < N) {
+                                    uint32_t wd = selbits[b * nwords + (bit0 >> 5)];
+                                    const int valid = min(32, N - bit0);
+                                    if (valid < 32) wd &= (1u << valid) - 1u;
+                                    ones += __popc(wd);
+                                }
                             }
+                            if (ones < cnt) part |= 1u << b;
                         }
-                        need = ones < cnt;
                     }
-                    const uint64_t m = __ballot(need);
-                    if (need) tiles[nt + __popcll(m & ((1ull << lane) - 1ull))] = kApprox | c;
+                    const uint64_t m = __ballot(part != 0);
+                    if (part) tiles[nt + __popcll(m & ((1ull << lane) - 1ull))] = kApprox | (part << kPartShift) | c;
                     nt += __popcll(m);
                 }
-                // exact tiles, ascending key block
+                // exact key blocks, ascending
                 for (int j0 = 0; j0 < N; j0 += 64) {
                     const int j = j0 + lane;
-                    const bool sel = j < N && ((selbits[j >> 5] >> (j & 31)) & 1u);
-                    const uint64_t m = __ballot(sel);
-                    if (sel) tiles[nt + __popcll(m & ((1ull << lane) - 1ull))] = j;
+                    uint32_t part = 0;
+                    if (j < N)
+                        for (int b = 0; b < nqb; ++b)
+                            part |= ((selbits[b * nwords + (j >> 5)] >> (j & 31)) & 1u) << b;
+                    const uint64_t m = __ballot(part != 0);
+                    if (part) tiles[nt + __popcll(m & ((1ull << lane) - 1ull))] = (part << kPartShift) | j;
                     nt += __popcll(m);
                 }
                 if (lane == 0) misc_s[1] = nt;
                 if (a.sel_dbg) {
-                    uint32_t* dst = a.sel_dbg + (size_t)item * a.W;
-                    for (int w = lane; w < nwords; w += 64) {
-                        uint32_t wd = selbits[w];
-                        const int valid = N - 32 * w;
-                        if (valid < 32) wd &= (1u << valid) - 1u;
-                        dst[w] = wd;
+                    for (int b = 0; b < nqb; ++b) {
+                        uint32_t* dst = a.sel_dbg + ((size_t)h * N + i0 + b) * a.W;
+                        for (int w = lane; w < nwords; w += 64) {
+                            uint32_t wd = selbits[b * nwords + w];
+                            const int valid = N - 32 * w;
+                            if (valid < 32) wd &= (1u << valid) - 1u;
+                            dst[w] = wd;
+                        }
                     }
                 }
             }
@@ -254,7 +242,7 @@ __global__ void __launch_bounds__(2 * BLK) sweep_bf16_kernel(AttnArgs a) {
             T = misc_s[1];
         }
 
-        // Q fragments (B operand of S^T = K Q^T): rows 32w + 16qt + l16
+        // Q fragments (B operand of S^T = K Q^T): rows q0 + 32w + 16qt + l16
         bf16x8_t qf[2][S::NS];
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
@@ -272,107 +260,84 @@ __global__ void __launch_bounds__(2 * BLK) sweep_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int dt = 0; dt < S::NDT; ++dt) o[dt][0] = o[dt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        auto tile_src = [&](int t, const u16*& kp, const u16*& vp, int& nvalid) {
-            const uint32_t desc = DENSE ? static_cast<uint32_t>(t) : tiles[t];
-            if (desc & kApprox) {
-                const int c = static_cast<int>(desc & ~kApprox);
-                const size_t off = ((size_t)h * N + (size_t)c * BLK) * D;
-                kp = a.kbar_bf + off;
-                vp = a.vsum_bf + off;
-                nvalid = min(BLK, N - c * BLK);
-            } else {
-                const int j = static_cast<int>(desc);
-                kp = kg + head_off + (size_t)j * BLK * D;
-                vp = vg + head_off + (size_t)j * BLK * D;
-                nvalid = min(BLK, L - j * BLK);
-            }
+        const uint32_t all_part = (1u << nqb) - 1u;
+        // entry of 64-key tile t: (approx?, part, row0 of the tile in its source)
+        auto entry = [&](int t, bool& approx, uint32_t& part, int& row0) {
+            const int e = t / S::SUB, sub = t % S::SUB;
+            const uint32_t d = DENSE ? ((all_part << kPartShift) | (uint32_t)e) : tiles[e];
+            approx = (d & kApprox) != 0;
+            part = (d >> kPartShift) & 3u;
+            row0 = (int)(d & kIndexMask) * BLK + sub * 64;
+        };
+        auto issue = [&](int t, u16* Kd, u16* Vd) {
+            bool ap;
+            uint32_t pt;
+            int row0;
+            entry(t, ap, pt, row0);
+            if (ap)
+                tile_issue<D, BLK>(a.kbar_bf + (size_t)h * N * D, a.vsum_bf + (size_t)h * N * D,
+                                   row0, N - 1, Kd, Vd, wave, lane);
+            else
+                tile_issue<D, BLK>(kg + head_off, vg + head_off, row0, L - 1, Kd, Vd, wave, lane);
         };
 
-        TileRegs<D, BLK> tr;
-        if (T > 0) {
-            const u16 *kp, *vp;
-            int nv;
-            tile_src(0, kp, vp, nv);
-            tile_load<D, BLK>(tr, kp, vp, nv, tid);
-        }
-        for (int t = 0; t < T; ++t) {
-            __syncthreads();  // the previous tile's readers are done with Ks / Vt
-            tile_store<D, BLK>(tr, Ks, Vt, tid);
-            __syncthreads();
-            const uint32_t desc = DENSE ? static_cast<uint32_t>(t) : tiles[t];
-            if (t + 1 < T) {
-                const u16 *kp, *vp;
-                int nv;
-                tile_src(t + 1, kp, vp, nv);
-                tile_load<D, BLK>(tr, kp, vp, nv, tid);
-            }
+        // compute tile t from (Kt, Vt) while tile t+1 streams into (Kn, Vn)
+        auto step = [&](int t, const u16* Kt, const u16* Vt, u16* Kn, u16* Vn, int TS) {
+            __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of tile t have landed
+            __syncthreads();                // everyone's have; tile t-1 is no longer read
+            if (t + 1 < TS) issue(t + 1, Kn, Vn);
+            bool approx;
+            uint32_t part;
+            int row0;
+            entry(t, approx, part, row0);
+            if (!((part >> myb) & 1u)) return;  // this wave's query block does not use it
 
             // S^T = K Q^T for this wave's 32 query rows
-            f32x4_t sacc[S::NKT][2];
+            f32x4_t sacc[4][2];
 #pragma unroll
-            for (int kt = 0; kt < S::NKT; ++kt) sacc[kt][0] = sacc[kt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int kt = 0; kt < 4; ++kt) sacc[kt][0] = sacc[kt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < S::NS; ++s) {
 #pragma unroll
-                for (int kt = 0; kt < S::NKT; ++kt) {
-                    const u32x4_t av =
-                        *reinterpret_cast<const u32x4_t*>(Ks + (kt * 16 + l16) * S::KP + s * 32 + g * 8);
+                for (int kt = 0; kt < 4; ++kt) {
+                    const int r = kt * 16 + l16;
+                    const u32x4_t av = *reinterpret_cast<const u32x4_t*>(
+                        Kt + r * D + (((s * 4 + g) ^ k_swz(r)) << 3));
                     sacc[kt][0] = mfma16(as_bf16x8(av), qf[0][s], sacc[kt][0]);
                     sacc[kt][1] = mfma16(as_bf16x8(av), qf[1][s], sacc[kt][1]);
                 }
             }
 
-            // masks and weights of this tile's BLK columns
-            const bool approx = (desc & kApprox) != 0;
-            int c0;
-            int nvalid;
-            uint64_t colsel = 0, colsel_hi = 0;  // approximate tile: columns computed exactly
+            // column masks: tokens past L (exact), selected or past-N pooled
+            // keys (approximate)
+            const int limit = approx ? N : L;
+            uint64_t colsel = 0;
             if (approx) {
-                const int c = static_cast<int>(desc & ~kApprox);
-                c0 = c * BLK;
-                nvalid = min(BLK, N - c0);
-#pragma unroll
-                for (int w32 = 0; w32 < 2; ++w32)
-                    if (c0 + 32 * w32 < N)
-                        colsel |= static_cast<uint64_t>(selbits[(c0 >> 5) + w32]) << (32 * w32);
-                if (BLK == 128) {
-#pragma unroll
-                    for (int w32 = 2; w32 < 4; ++w32)
-                        if (c0 + 32 * w32 < N)
-                            colsel_hi |= static_cast<uint64_t>(selbits[(c0 >> 5) + w32]) << (32 * (w32 - 2));
-                }
-            } else {
-                c0 = static_cast<int>(desc) * BLK;
-                nvalid = min(BLK, L - c0);
+                const uint32_t* sb = selbits + myb * nwords;
+                if (row0 < N) colsel = sb[row0 >> 5];
+                if (row0 + 32 < N) colsel |= static_cast<uint64_t>(sb[(row0 >> 5) + 1]) << 32;
             }
-            if (approx || nvalid < BLK) {
-                // masked columns -> -inf (raw score units; the scale is positive)
+            if (approx || row0 + 64 > limit) {
 #pragma unroll
-                for (int kt = 0; kt < S::NKT; ++kt) {
+                for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const int jj = kt * 16 + g * 4 + r;
-                        bool valid = jj < nvalid;
-                        if (approx) {
-                            const uint64_t cs = jj < 64 ? colsel : colsel_hi;
-                            valid = valid && !((cs >> (jj & 63)) & 1ull);
-                        }
+                        const bool valid = row0 + jj < limit && !((colsel >> jj) & 1ull);
                         if (!valid) sacc[kt][0][r] = sacc[kt][1][r] = -INFINITY;
                     }
-                }
             }
 
-            // Online softmax in base 2 with a lazily raised reference max:
-            // the reference m only moves when a row's max exceeds it by more
-            // than 8 (so every weight stays <= 2^8); any reference cancels in
-            // out = O / l.
+            // online softmax in base 2 with a lazily raised reference max
+            // (it moves only when a row max exceeds it by more than 8, so
+            // every weight stays <= 2^8; any reference cancels in O / l)
             const float cl2 = a.c_log2e;
             float mx[2];
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
                 float v = -INFINITY;
 #pragma unroll
-                for (int kt = 0; kt < S::NKT; ++kt)
+                for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) v = fmaxf(v, sacc[kt][qt][r]);
                 mx[qt] = max4rows(v) * cl2;
@@ -401,9 +366,9 @@ __global__ void __launch_bounds__(2 * BLK) sweep_bf16_kernel(AttnArgs a) {
                     // Eq. (9): a pooled key stands for n_j tokens
                     const float wlast = static_cast<float>(a.nlast);
                     const float wblk = static_cast<float>(BLK);
-                    const int jlast = N - 1 - c0;
+                    const int jlast = N - 1 - row0;
 #pragma unroll
-                    for (int kt = 0; kt < S::NKT; ++kt)
+                    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][qt][r], cl2, neg_m));
@@ -412,7 +377,7 @@ __global__ void __launch_bounds__(2 * BLK) sweep_bf16_kernel(AttnArgs a) {
                         }
                 } else {
 #pragma unroll
-                    for (int kt = 0; kt < S::NKT; ++kt)
+                    for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {
                             const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][qt][r], cl2, neg_m));
@@ -425,8 +390,11 @@ __global__ void __launch_bounds__(2 * BLK) sweep_bf16_kernel(AttnArgs a) {
 
             // O^T += V^T P^T.  k-index 8g+e of 32-key step u is key 32u + 4g + e
             // (e < 4) or 32u + 16 + 4g + (e - 4): the keys this lane holds.
+            // The transposing read gives lane (l16, g) four keys of column
+            // d = 16 dt + l16 from the row addresses of lanes 16g + p + 4e.
+            const int tp = l16 & 3, te = l16 >> 2;
 #pragma unroll
-            for (int u = 0; u < S::NU; ++u) {
+            for (int u = 0; u < 2; ++u) {
                 u32x4_t pb[2];
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt)
@@ -434,33 +402,46 @@ __global__ void __launch_bounds__(2 * BLK) sweep_bf16_kernel(AttnArgs a) {
                                      pack_bf16x2(sacc[2 * u][qt][2], sacc[2 * u][qt][3]),
                                      pack_bf16x2(sacc[2 * u + 1][qt][0], sacc[2 * u + 1][qt][1]),
                                      pack_bf16x2(sacc[2 * u + 1][qt][2], sacc[2 * u + 1][qt][3])};
+                const int key_lo = 32 * u + 4 * g + te;  // v_swz(key) = 2 te
 #pragma unroll
                 for (int dt = 0; dt < S::NDT; ++dt) {
-                    const int d = dt * 16 + l16;
-                    const u16* vr = Vt + d * S::VP;
-                    const int sw = vt_swz(d);
-                    const u32x2_t lo = *reinterpret_cast<const u32x2_t*>(vr + (((8 * u + g) ^ sw) << 2));
-                    const u32x2_t hi = *reinterpret_cast<const u32x2_t*>(vr + (((8 * u + 4 + g) ^ sw) << 2));
-                    const bf16x8_t av = as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]});
+                    const int ch = (2 * dt + (tp >> 1)) ^ (te << 1);
+                    const int off = ch * 8 + 4 * (tp & 1);
+                    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4_t*)(Vt + key_lo * D + off));
+                    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4_t*)(Vt + (key_lo + 16) * D + off));
+                    const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
+                    const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
+                    const bf16x8_t av = as_bf16x8(u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]});
                     o[dt][0] = mfma16(av, as_bf16x8(pb[0]), o[dt][0]);
                     o[dt][1] = mfma16(av, as_bf16x8(pb[1]), o[dt][1]);
                 }
             }
+        };
+
+        const int TS = T * S::SUB;
+        if (TS > 0) issue(0, K0, V0);
+        for (int t = 0; t < TS; t += 2) {
+            step(t, K0, V0, K1, V1, TS);
+            if (t + 1 < TS) step(t + 1, K1, V1, K0, V0, TS);
         }
 
         // ---- 3. out_r = N_r / D_r --------------------------------------------
+        if (myb < nqb) {
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            const float lt = sum4rows(l_run[qt]);
-            const float inv = 1.0f / lt;
-            const int row = q0 + wave * 32 + qt * 16 + l16;
-            if (row < L) {
-                u16* dst = og + head_off + (size_t)row * D + g * 4;
+            for (int qt = 0; qt < 2; ++qt) {
+                const float lt = sum4rows(l_run[qt]);
+                const float inv = 1.0f / lt;
+                const int row = q0 + wave * 32 + qt * 16 + l16;
+                if (row < L) {
+                    u16* dst = og + head_off + (size_t)row * D + g * 4;
 #pragma unroll
-                for (int dt = 0; dt < S::NDT; ++dt) {
-                    const u32x2_t pk = {pack_bf16x2(o[dt][qt][0] * inv, o[dt][qt][1] * inv),
-                                        pack_bf16x2(o[dt][qt][2] * inv, o[dt][qt][3] * inv)};
-                    *reinterpret_cast<u32x2_t*>(dst + dt * 16) = pk;
+                    for (int dt = 0; dt < S::NDT; ++dt) {
+                        const u32x2_t pk = {pack_bf16x2(o[dt][qt][0] * inv, o[dt][qt][1] * inv),
+                                            pack_bf16x2(o[dt][qt][2] * inv, o[dt][qt][3] * inv)};
+                        *reinterpret_cast<u32x2_t*>(dst + dt * 16) = pk;
+                    }
                 }
             }
         }
@@ -486,10 +467,11 @@ hipError_t sweep_t(const AttnArgs& a, hipStream_t s) {
     using S = Sweep<D, BLK>;
     auto kern = sweep_bf16_kernel<D, BLK, DENSE>;
     const int NC = (a.N + BLK - 1) / BLK;
-    const size_t dyn = DENSE ? 0 : sizeof(uint32_t) * ((size_t)(a.N + 31) / 32 + NC + a.N);
+    const size_t dyn = DENSE ? 0 : sizeof(uint32_t) * ((size_t)S::QB * ((a.N + 31) / 32) + NC + a.N);
     int grid;
     if (DENSE) {
-        grid = 8 * ((a.H * a.N + 7) / 8);
+        const int NG = (a.N + S::QB - 1) / S::QB;
+        grid = 8 * ((a.H * NG + 7) / 8);
     } else {
         int per_cu = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, S::NT, dyn) != hipSuccess ||
@@ -502,11 +484,6 @@ hipError_t sweep_t(const AttnArgs& a, hipStream_t s) {
 }
 
 }  // namespace
-
-size_t sweep_dynamic_lds(int N, int B) {
-    const int NC = (N + B - 1) / B;
-    return sizeof(uint32_t) * ((size_t)(N + 31) / 32 + NC + N);
-}
 
 hipError_t launch_sweep_bf16(const AttnArgs& a, int d, int B, bool dense, hipStream_t s) {
     if (d == 64 && B == 64) return dense ? sweep_t<64, 64, true>(a, s) : sweep_t<64, 64, false>(a, s);
