@@ -96,10 +96,19 @@ __device__ __forceinline__ void load_kbar_quarter(const float* __restrict__ row,
     }
 }
 
+// qbar in LDS is stored in four quarters of D/4 floats at a stride of
+// QSTRIDE = D/4 + 1, so the four lanes of a key read four different banks.
+template <int D>
+struct QbarLds {
+    static constexpr int QSTRIDE = D / 4 + 1;
+    static constexpr int SIZE = 4 * QSTRIDE;
+    __device__ static int index(int x) { return (x / (D / 4)) * QSTRIDE + (x % (D / 4)); }
+};
+
 template <int D>
 __device__ __forceinline__ float proxy_from_quarter(const float* qbar_lds, const float (&kv)[D / 4],
                                                     int qq, float scale) {
-    const float* qp = qbar_lds + qq * (D / 4);
+    const float* qp = qbar_lds + qq * QbarLds<D>::QSTRIDE;
     float acc = 0.0f;
 #pragma unroll
     for (int e = 0; e < D / 4; ++e) acc = __builtin_fmaf(qp[e], kv[e], acc);

@@ -22,7 +22,7 @@ __global__ void __launch_bounds__(4 * BLK) attn_f32_kernel(AttnArgs a) {
     constexpr int KP = D + 4;  // pitch keeps 16-byte alignment
     __shared__ __align__(16) float Kf[BLK * KP];
     __shared__ __align__(16) float Vf[BLK * KP];
-    __shared__ __align__(16) float qb_s[D];
+    __shared__ __align__(16) float qb_s[QbarLds<D>::SIZE];
     __shared__ float wt_s[BLK];            // column weight; 0 = masked column
     __shared__ int sel_list[BLK];
     __shared__ unsigned char flag_s[BLK];
@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(4 * BLK) attn_f32_kernel(AttnArgs a) {
         }
         float tau_i = 0.0f;
         if (!DENSE) {
-            for (int t = tid; t < D; t += NT) qb_s[t] = a.qbar[(size_t)item * D + t];
+            for (int t = tid; t < D; t += NT) qb_s[QbarLds<D>::index(t)] = a.qbar[(size_t)item * D + t];
             tau_i = a.tau[item];
         }
         float m_run = -INFINITY, l_run = 0.0f;

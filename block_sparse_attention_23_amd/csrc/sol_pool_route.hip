@@ -141,7 +141,7 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
                                                     int32_t* __restrict__ kept,
                                                     int* __restrict__ queues) {
     extern __shared__ float rows[];  // [R][N]
-    __shared__ float qb[R][D];
+    __shared__ float qb[R][QbarLds<D>::SIZE];
     const int h = blockIdx.x / groups_per_head;
     const int i0 = (blockIdx.x % groups_per_head) * R;
     const int nr = min(R, N - i0);
@@ -149,7 +149,7 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
     if (queues && blockIdx.x == 0 && tid < 8) queues[tid] = 0;
     for (int t = tid; t < R * D; t += 256) {
         const int r = t / D, x = t % D;
-        qb[r][x] = r < nr ? qbar[((size_t)h * N + i0 + r) * D + x] : 0.0f;
+        qb[r][QbarLds<D>::index(x)] = r < nr ? qbar[((size_t)h * N + i0 + r) * D + x] : 0.0f;
     }
     __syncthreads();
 
@@ -231,7 +231,7 @@ template <int D>
 hipError_t route_d(const float* qbar, const float* kbar, int H, int N, float c, float beta,
                    float* tau, int32_t* kept, int* queues, hipStream_t s) {
     // as many rows per workgroup as 64 KB of LDS holds
-    const size_t row_bytes = sizeof(float) * ((size_t)N + D);
+    const size_t row_bytes = sizeof(float) * ((size_t)N + QbarLds<D>::SIZE);
     if (16 * row_bytes <= 65536) return route_t<D, 16>(qbar, kbar, H, N, c, beta, tau, kept, queues, s);
     if (8 * row_bytes <= 65536) return route_t<D, 8>(qbar, kbar, H, N, c, beta, tau, kept, queues, s);
     if (4 * row_bytes <= 65536) return route_t<D, 4>(qbar, kbar, H, N, c, beta, tau, kept, queues, s);

@@ -64,11 +64,16 @@ constexpr uint32_t kApprox = 0x80000000u;  // tile-list entry: approximate chunk
 constexpr int kPartShift = 29;             // bits 29..30: query blocks using the entry
 constexpr uint32_t kIndexMask = (1u << kPartShift) - 1u;
 
-// K tiles: 16-byte chunk c of row r sits at position c ^ (r & 7); V tiles at
-// c ^ 2 (r & 3).  Both make the MFMA operand reads (b128 rows for K, the
-// transposing b64 read for V) hit 32 distinct banks.
-__device__ __forceinline__ int k_swz(int r) { return r & 7; }
-__device__ __forceinline__ int v_swz(int r) { return (r & 3) << 1; }
+// LDS swizzles (the 16-byte chunk c of tile row r is stored at c ^ swz(r)),
+// chosen by measuring SQ_LDS_BANK_CONFLICT on gfx950: a b128 read serves 16
+// lanes per cycle, the transposing b64 read 32, over 64 four-byte banks.
+// K rows: the 16 rows read together must cover 16 distinct 16-byte slots.
+// V rows: the 8 key rows x 4 column chunks read together by the transposing
+// read must cover 32 distinct 8-byte slots.
+template <int D>
+__device__ __forceinline__ int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int v_swz(int r) { return D == 128 ? ((r & 7) << 1) : (((r >> 1) & 3) << 1); }
 
 // Keep bits 0, 4, 8, ..., 60 of m and pack them into bits 0..15.
 __device__ __forceinline__ uint32_t every_fourth_bit(uint64_t m) {
@@ -80,25 +85,53 @@ __device__ __forceinline__ uint32_t every_fourth_bit(uint64_t m) {
     return static_cast<uint32_t>(x);
 }
 
-// Issue the direct-to-LDS loads of one 64-row tile: rows row0 .. row0+63 of
-// the K-like and V-like sources (row stride D, rows past rowmax repeat
-// rowmax -- their columns are masked).  Wave w fills 1 KB blocks w*LPT ..
-// w*LPT+LPT-1; lane l writes the 16 bytes at block + 16 l.
+// Per-lane parts of the direct-to-LDS loads of a 64-row tile, fixed for the
+// kernel: load i of this lane fetches tile row r[i], 16-byte chunk
+// (lane % CH) ^ swz(r[i]) of the source, into 1 KB LDS block wave*LPT + i
+// (lane l writes bytes 16 l .. 16 l + 15 of the block).
 template <int D, int BLK>
-__device__ __forceinline__ void tile_issue(const u16* __restrict__ kp, const u16* __restrict__ vp,
-                                           int row0, int rowmax, u16* Kdst, u16* Vdst, int wave,
-                                           int lane) {
+struct TileLanes {
+    int r[Sweep<D, BLK>::LPT];
+    uint32_t koff[Sweep<D, BLK>::LPT];  // r * D + swizzled chunk (elements)
+    uint32_t voff[Sweep<D, BLK>::LPT];
+};
+
+template <int D, int BLK>
+__device__ __forceinline__ void tile_lanes_init(TileLanes<D, BLK>& tl, int wave, int lane) {
     using S = Sweep<D, BLK>;
 #pragma unroll
     for (int i = 0; i < S::LPT; ++i) {
-        const int bi = wave * S::LPT + i;
-        const int r = bi * S::RPK + lane / S::CH;
+        const int r = (wave * S::LPT + i) * S::RPK + lane / S::CH;
         const int ph = lane % S::CH;
-        const size_t srow = (size_t)min(row0 + r, rowmax) * D;
-        __builtin_amdgcn_global_load_lds(kp + srow + ((ph ^ k_swz(r)) << 3),
-                                         (lds_void_t*)(Kdst + bi * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vp + srow + ((ph ^ v_swz(r)) << 3),
-                                         (lds_void_t*)(Vdst + bi * 512), 16, 0, 0);
+        tl.r[i] = r;
+        tl.koff[i] = (uint32_t)(r * D + ((ph ^ k_swz<D>(r)) << 3));
+        tl.voff[i] = (uint32_t)(r * D + ((ph ^ v_swz<D>(r)) << 3));
+    }
+}
+
+// Issue the direct-to-LDS loads of one 64-row tile: rows row0 .. row0+63 of
+// the K-like and V-like sources (row stride D); rows past rowmax repeat
+// rowmax (their columns are masked).  wave_s is the wave index in an SGPR.
+template <int D, int BLK>
+__device__ __forceinline__ void tile_issue(const u16* __restrict__ kp, const u16* __restrict__ vp,
+                                           int row0, int rowmax, u16* Kdst, u16* Vdst, int wave_s,
+                                           const TileLanes<D, BLK>& tl) {
+    using S = Sweep<D, BLK>;
+    const bool full = row0 + 64 <= rowmax + 1;
+    const uint32_t base = (uint32_t)row0 * D;
+#pragma unroll
+    for (int i = 0; i < S::LPT; ++i) {
+        uint32_t ko = base + tl.koff[i], vo = base + tl.voff[i];
+        if (!full) {
+            const int over = row0 + tl.r[i] - rowmax;
+            if (over > 0) {
+                ko -= (uint32_t)over * D;
+                vo -= (uint32_t)over * D;
+            }
+        }
+        const int blk = (wave_s * S::LPT + i) * 512;
+        __builtin_amdgcn_global_load_lds(kp + ko, (lds_void_t*)(Kdst + blk), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vp + vo, (lds_void_t*)(Vdst + blk), 16, 0, 0);
     }
 }
 
@@ -111,7 +144,7 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
     __shared__ __align__(16) u16 V0[S::TILE];
     __shared__ __align__(16) u16 K1[S::TILE];
     __shared__ __align__(16) u16 V1[S::TILE];
-    __shared__ __align__(16) float qb_s[S::QB][D];
+    __shared__ __align__(16) float qb_s[S::QB][QbarLds<D>::SIZE];
     __shared__ float tau_s[S::QB];
     __shared__ int misc_s[2];
     extern __shared__ __align__(16) uint32_t dyn[];  // selection bits per block, then tile list
@@ -129,6 +162,9 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
     uint32_t* selbits = dyn;                 // [QB][nwords]
     uint32_t* tiles = dyn + S::QB * nwords;  // up to NC + N entries
     const int myb = (wave * 32) / BLK;       // this wave's query block within the group
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    TileLanes<D, BLK> tl;
+    tile_lanes_init<D, BLK>(tl, wave, lane);
 
     int dense_item = -1;
     if (DENSE) {
@@ -163,7 +199,7 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             // ---- 1. routing on chip --------------------------------------
             for (int t = tid; t < S::QB * D; t += S::NT) {
                 const int b = t / D, x = t % D;
-                qb_s[b][x] = b < nqb ? a.qbar[((size_t)h * N + i0 + b) * D + x] : 0.0f;
+                qb_s[b][QbarLds<D>::index(x)] = b < nqb ? a.qbar[((size_t)h * N + i0 + b) * D + x] : 0.0f;
             }
             if (tid < S::QB) tau_s[tid] = tid < nqb ? a.tau[(size_t)h * N + i0 + tid] : INFINITY;
             __syncthreads();
@@ -255,10 +291,17 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
         }
 
         // ---- 2. the tile loop ---------------------------------------------
-        float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.0f, 0.0f};
-        f32x4_t o[S::NDT][2];
+        // o[0..NDT-1]: O^T tiles; o[NDT]: the softmax denominator, formed by
+        // the MFMA from a weight row (row 0 of an extra 16-row V^T tile holds
+        // each key's weight: 1 per token, n_j per pooled key -- Eq. (9)), so
+        // numerator and denominator use the same bf16-rounded weights.
+        float m_run[2] = {-INFINITY, -INFINITY};
+        f32x4_t o[S::NDT + 1][2];
 #pragma unroll
-        for (int dt = 0; dt < S::NDT; ++dt) o[dt][0] = o[dt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int dt = 0; dt <= S::NDT; ++dt) o[dt][0] = o[dt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // weight-row operands: lanes with l16 == 0 carry row 0 (8 keys each)
+        const uint32_t one2 = l16 == 0 ? 0x3F803F80u : 0u;  // bf16 1.0, 1.0
+        const uint32_t blk2 = l16 == 0 ? pack_bf16x2(static_cast<float>(BLK), static_cast<float>(BLK)) : 0u;
 
         const uint32_t all_part = (1u << nqb) - 1u;
         // entry of 64-key tile t: (approx?, part, row0 of the tile in its source)
@@ -276,9 +319,9 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             entry(t, ap, pt, row0);
             if (ap)
                 tile_issue<D, BLK>(a.kbar_bf + (size_t)h * N * D, a.vsum_bf + (size_t)h * N * D,
-                                   row0, N - 1, Kd, Vd, wave, lane);
+                                   row0, N - 1, Kd, Vd, wave_s, tl);
             else
-                tile_issue<D, BLK>(kg + head_off, vg + head_off, row0, L - 1, Kd, Vd, wave, lane);
+                tile_issue<D, BLK>(kg + head_off, vg + head_off, row0, L - 1, Kd, Vd, wave_s, tl);
         };
 
         // compute tile t from (Kt, Vt) while tile t+1 streams into (Kn, Vn)
@@ -292,20 +335,34 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             entry(t, approx, part, row0);
             if (!((part >> myb) & 1u)) return;  // this wave's query block does not use it
 
-            // S^T = K Q^T for this wave's 32 query rows
+            // S^T = K Q^T for this wave's 32 query rows, in batches of KB
+            // k-steps: the batch's K fragments are read first (LDS reads in
+            // flight together), then the MFMAs consume them.
+            constexpr int KB = S::NS >= 2 ? 2 : 1;
             f32x4_t sacc[4][2];
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt) sacc[kt][0] = sacc[kt][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            for (int s0 = 0; s0 < S::NS; s0 += KB) {
+                u32x4_t kfr[KB][4];
 #pragma unroll
-            for (int s = 0; s < S::NS; ++s) {
+                for (int sb = 0; sb < KB; ++sb)
 #pragma unroll
-                for (int kt = 0; kt < 4; ++kt) {
-                    const int r = kt * 16 + l16;
-                    const u32x4_t av = *reinterpret_cast<const u32x4_t*>(
-                        Kt + r * D + (((s * 4 + g) ^ k_swz(r)) << 3));
-                    sacc[kt][0] = mfma16(as_bf16x8(av), qf[0][s], sacc[kt][0]);
-                    sacc[kt][1] = mfma16(as_bf16x8(av), qf[1][s], sacc[kt][1]);
+                    for (int kt = 0; kt < 4; ++kt) {
+                        const int r = kt * 16 + l16;
+                        kfr[sb][kt] = *reinterpret_cast<const u32x4_t*>(
+                            Kt + r * D + ((((s0 + sb) * 4 + g) ^ k_swz<D>(r)) << 3));
+                    }
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int sb = 0; sb < KB; ++sb) {
+#pragma unroll
+                    for (int kt = 0; kt < 4; ++kt) {
+                        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+                        const int s = s0 + sb;
+                        sacc[kt][0] = mfma16(as_bf16x8(kfr[sb][kt]), qf[0][s], s == 0 ? z : sacc[kt][0]);
+                        sacc[kt][1] = mfma16(as_bf16x8(kfr[sb][kt]), qf[1][s], s == 0 ? z : sacc[kt][1]);
+                    }
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
 
             // column masks: tokens past L (exact), selected or past-N pooled
@@ -350,10 +407,9 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                     const float m_new = fmaxf(m_run[qt], mx[qt]);
                     alpha[qt] = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run[qt] - m_new);
                     m_run[qt] = m_new;
-                    l_run[qt] *= alpha[qt];
                 }
 #pragma unroll
-                for (int dt = 0; dt < S::NDT; ++dt) {
+                for (int dt = 0; dt <= S::NDT; ++dt) {
                     o[dt][0] *= alpha[0];
                     o[dt][1] *= alpha[1];
                 }
@@ -361,31 +417,35 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
                 const float neg_m = m_run[qt] == -INFINITY ? 0.0f : -m_run[qt];
-                float psum = 0.0f;
-                if (approx) {
-                    // Eq. (9): a pooled key stands for n_j tokens
-                    const float wlast = static_cast<float>(a.nlast);
-                    const float wblk = static_cast<float>(BLK);
-                    const int jlast = N - 1 - row0;
 #pragma unroll
-                    for (int kt = 0; kt < 4; ++kt)
+                for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][qt][r], cl2, neg_m));
-                            sacc[kt][qt][r] = p;
-                            psum = __builtin_fmaf((kt * 16 + g * 4 + r == jlast) ? wlast : wblk, p, psum);
-                        }
-                } else {
+                    for (int r = 0; r < 4; ++r)
+                        sacc[kt][qt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][qt][r], cl2, neg_m));
+            }
+
+            // weight row of this tile: 1 per token; n_j per pooled key (B, or
+            // n_last for the ragged last block when this tile holds it)
+            u32x4_t wrow[2];
+            {
+                const uint32_t w2 = approx ? blk2 : one2;
+                wrow[0] = wrow[1] = u32x4_t{w2, w2, w2, w2};
+                const int jlast = N - 1 - row0;
+                if (approx && a.nlast != BLK && jlast >= 0 && jlast < 64 && l16 == 0) {
+                    // k-index 8g+e of step u is key 32u + 4g + e or 32u + 16 + 4g + e - 4
+                    const int u = jlast >> 5, rem = jlast & 31;
+                    const int gl = (rem & 15) >> 2, e = (rem & 3) + (rem >= 16 ? 4 : 0);
+                    if (g == gl) {
+                        u16 wv[8];
 #pragma unroll
-                    for (int kt = 0; kt < 4; ++kt)
+                        for (int x = 0; x < 8; ++x) wv[x] = static_cast<u16>(blk2 & 0xFFFFu);
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kt][qt][r], cl2, neg_m));
-                            sacc[kt][qt][r] = p;
-                            psum += p;
-                        }
+                        for (int x = 0; x < 8; ++x)
+                            if (x == e) wv[x] = static_cast<u16>(pack_bf16x2(static_cast<float>(a.nlast), 0.f) & 0xFFFFu);
+                        wrow[u] = u32x4_t{wv[0] | (uint32_t(wv[1]) << 16), wv[2] | (uint32_t(wv[3]) << 16),
+                                          wv[4] | (uint32_t(wv[5]) << 16), wv[6] | (uint32_t(wv[7]) << 16)};
+                    }
                 }
-                l_run[qt] += psum;
             }
 
             // O^T += V^T P^T.  k-index 8g+e of 32-key step u is key 32u + 4g + e
@@ -395,6 +455,8 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             const int tp = l16 & 3, te = l16 >> 2;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
+                const int key_lo = 32 * u + 4 * g + te;  // v_swz(key_lo + 16) == v_swz(key_lo)
+                const int vs = v_swz<D>(key_lo);
                 u32x4_t pb[2];
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt)
@@ -402,21 +464,32 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                                      pack_bf16x2(sacc[2 * u][qt][2], sacc[2 * u][qt][3]),
                                      pack_bf16x2(sacc[2 * u + 1][qt][0], sacc[2 * u + 1][qt][1]),
                                      pack_bf16x2(sacc[2 * u + 1][qt][2], sacc[2 * u + 1][qt][3])};
-                const int key_lo = 32 * u + 4 * g + te;  // v_swz(key) = 2 te
+                // V^T operands in batches of VB d-tiles of transposing reads
+                constexpr int VB = S::NDT >= 4 ? 4 : S::NDT;
 #pragma unroll
-                for (int dt = 0; dt < S::NDT; ++dt) {
-                    const int ch = (2 * dt + (tp >> 1)) ^ (te << 1);
-                    const int off = ch * 8 + 4 * (tp & 1);
-                    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_s16x4_t*)(Vt + key_lo * D + off));
-                    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (lds_s16x4_t*)(Vt + (key_lo + 16) * D + off));
-                    const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo);
-                    const u32x2_t hi2 = __builtin_bit_cast(u32x2_t, hi);
-                    const bf16x8_t av = as_bf16x8(u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]});
-                    o[dt][0] = mfma16(av, as_bf16x8(pb[0]), o[dt][0]);
-                    o[dt][1] = mfma16(av, as_bf16x8(pb[1]), o[dt][1]);
+                for (int d0 = 0; d0 < S::NDT; d0 += VB) {
+                    bf16x8_t vfr[VB];
+#pragma unroll
+                    for (int db = 0; db < VB; ++db) {
+                        const int dt = d0 + db;
+                        const int ch = (2 * dt + (tp >> 1)) ^ vs;
+                        const int off = ch * 8 + 4 * (tp & 1);
+                        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_s16x4_t*)(Vt + key_lo * D + off));
+                        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_s16x4_t*)(Vt + (key_lo + 16) * D + off));
+                        vfr[db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int db = 0; db < VB; ++db) {
+                        o[d0 + db][0] = mfma16(vfr[db], as_bf16x8(pb[0]), o[d0 + db][0]);
+                        o[d0 + db][1] = mfma16(vfr[db], as_bf16x8(pb[1]), o[d0 + db][1]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
+                o[S::NDT][0] = mfma16(as_bf16x8(wrow[u]), as_bf16x8(pb[0]), o[S::NDT][0]);
+                o[S::NDT][1] = mfma16(as_bf16x8(wrow[u]), as_bf16x8(pb[1]), o[S::NDT][1]);
             }
         };
 
@@ -431,7 +504,8 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
         if (myb < nqb) {
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
-                const float lt = sum4rows(l_run[qt]);
+                // row 0 of the weight tile sits in element 0 of lanes 0..15
+                const float lt = __shfl(o[S::NDT][qt][0], l16);
                 const float inv = 1.0f / lt;
                 const int row = q0 + wave * 32 + qt * 16 + l16;
                 if (row < L) {
