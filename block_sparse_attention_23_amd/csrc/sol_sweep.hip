@@ -85,14 +85,13 @@ __device__ __forceinline__ uint32_t every_fourth_bit(uint64_t m) {
     return static_cast<uint32_t>(x);
 }
 
-// Per-lane parts of the direct-to-LDS loads of a 64-row tile, fixed for the
-// kernel: load i of this lane fetches tile row r[i], 16-byte chunk
-// (lane % CH) ^ swz(r[i]) of the source, into 1 KB LDS block wave*LPT + i
-// (lane l writes bytes 16 l .. 16 l + 15 of the block).
+// Per-lane byte offsets of the direct-to-LDS loads of a 64-row tile, fixed
+// for the kernel: load i of this lane fetches tile row
+// r = (wave*LPT + i)*RPK + lane/CH, 16-byte chunk (lane % CH) ^ swz(r), into
+// 1 KB LDS block wave*LPT + i (lane l writes bytes 16 l .. 16 l + 15).
 template <int D, int BLK>
 struct TileLanes {
-    int r[Sweep<D, BLK>::LPT];
-    uint32_t koff[Sweep<D, BLK>::LPT];  // r * D + swizzled chunk (elements)
+    uint32_t koff[Sweep<D, BLK>::LPT];
     uint32_t voff[Sweep<D, BLK>::LPT];
 };
 
@@ -103,35 +102,61 @@ __device__ __forceinline__ void tile_lanes_init(TileLanes<D, BLK>& tl, int wave,
     for (int i = 0; i < S::LPT; ++i) {
         const int r = (wave * S::LPT + i) * S::RPK + lane / S::CH;
         const int ph = lane % S::CH;
-        tl.r[i] = r;
-        tl.koff[i] = (uint32_t)(r * D + ((ph ^ k_swz<D>(r)) << 3));
-        tl.voff[i] = (uint32_t)(r * D + ((ph ^ v_swz<D>(r)) << 3));
+        tl.koff[i] = (uint32_t)(2 * (r * D + ((ph ^ k_swz<D>(r)) << 3)));
+        tl.voff[i] = (uint32_t)(2 * (r * D + ((ph ^ v_swz<D>(r)) << 3)));
     }
 }
 
-// Issue the direct-to-LDS loads of one 64-row tile: rows row0 .. row0+63 of
-// the K-like and V-like sources (row stride D); rows past rowmax repeat
-// rowmax (their columns are masked).  wave_s is the wave index in an SGPR.
+// Buffer resources of one 64-row tile: rows row0 .. row0+63 of a source with
+// row stride D, limited to the rows before `rows` so that loads of rows past
+// the end return zero (their columns are masked).
+// (The buffer-resource type exists only in the device compilation.)
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+#else
+typedef void* rsrc_t;
+#endif
+struct TileSrc {
+    rsrc_t k, v;
+};
+
+// A pointer that is the same in every lane, moved to scalar registers.
+__device__ __forceinline__ void* uniform_ptr(const void* p) {
+    const uint64_t x = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
+    return reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+}
+
+template <int D>
+__device__ __forceinline__ TileSrc tile_src(const u16* kp, const u16* vp, int row0, int rows) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int kRawBuffer = 0x00020000;  // dword 3 of a raw (untyped) buffer resource
+    // With B = 128 a key block is two 64-row tiles, and the second can start
+    // at or past the end of its source (an approximate chunk's upper half
+    // when N <= 64 + 128 c, or an exact block holding <= 64 tokens): its
+    // range is then 0 bytes and every load of it is dropped.
+    const int nbytes = __builtin_amdgcn_readfirstlane(max(0, min(64, rows - row0)) * D * 2);
+    return TileSrc{__builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kp + (size_t)row0 * D), 0, nbytes, kRawBuffer),
+                   __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vp + (size_t)row0 * D), 0, nbytes, kRawBuffer)};
+#else
+    return TileSrc{};
+#endif
+}
+
+// Issue this wave's LPT pairs of direct-to-LDS loads (one K, one V) of a
+// tile.  wave_s is the wave index in an SGPR.
 template <int D, int BLK>
-__device__ __forceinline__ void tile_issue(const u16* __restrict__ kp, const u16* __restrict__ vp,
-                                           int row0, int rowmax, u16* Kdst, u16* Vdst, int wave_s,
+__device__ __forceinline__ void tile_issue(const TileSrc& src, u16* Kdst, u16* Vdst, int wave_s,
                                            const TileLanes<D, BLK>& tl) {
     using S = Sweep<D, BLK>;
-    const bool full = row0 + 64 <= rowmax + 1;
-    const uint32_t base = (uint32_t)row0 * D;
 #pragma unroll
     for (int i = 0; i < S::LPT; ++i) {
-        uint32_t ko = base + tl.koff[i], vo = base + tl.voff[i];
-        if (!full) {
-            const int over = row0 + tl.r[i] - rowmax;
-            if (over > 0) {
-                ko -= (uint32_t)over * D;
-                vo -= (uint32_t)over * D;
-            }
-        }
+#if defined(__HIP_DEVICE_COMPILE__)
         const int blk = (wave_s * S::LPT + i) * 512;
-        __builtin_amdgcn_global_load_lds(kp + ko, (lds_void_t*)(Kdst + blk), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vp + vo, (lds_void_t*)(Vdst + blk), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, (lds_void_t*)(Kdst + blk), 16, tl.koff[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void_t*)(Vdst + blk), 16, tl.voff[i], 0, 0, 0);
+#endif
     }
 }
 
@@ -153,7 +178,8 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
     const u16* __restrict__ kg = static_cast<const u16*>(a.k);
     const u16* __restrict__ vg = static_cast<const u16*>(a.v);
     u16* __restrict__ og = static_cast<u16*>(a.out);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform within a wave
     const int l16 = lane & 15, g = lane >> 4;
     const int H = a.H, L = a.L, N = a.N;
     const int NC = (N + BLK - 1) / BLK;
@@ -165,6 +191,34 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     TileLanes<D, BLK> tl;
     tile_lanes_init<D, BLK>(tl, wave, lane);
+    // per-lane LDS read offsets (elements), fixed for the kernel; the other
+    // parts of each read address (16-key tile, 32-key step, buffer) are
+    // compile-time constants.  K: 16-byte chunk 4s+g of key row l16 for
+    // 32-deep step s.  V: the transposing read of d tile dt for key row
+    // 4g + (l16 >> 2), column chunk 2dt + ((l16 & 3) >> 1), 8-byte half l16 & 1.
+    uint32_t koff_s[S::NS], voff_d[S::NDT];
+#pragma unroll
+    for (int s = 0; s < S::NS; ++s) koff_s[s] = (uint32_t)(l16 * D + (((s * 4 + g) ^ k_swz<D>(l16)) << 3));
+    {
+        const int tp = l16 & 3, key = 4 * g + (l16 >> 2);
+        const int vs = v_swz<D>(key);
+#pragma unroll
+        for (int dt = 0; dt < S::NDT; ++dt)
+            voff_d[dt] = (uint32_t)(key * D + (((2 * dt + (tp >> 1)) ^ vs) << 3) + 4 * (tp & 1));
+    }
+
+    // The tile buffers start zeroed: a direct-to-LDS load of a row past the
+    // end of its source is dropped by the buffer range check, so such rows
+    // hold zeros or rows of an earlier tile -- finite values in masked
+    // columns, whose weights are exactly zero.
+    for (int x = tid; x < S::TILE / 8; x += S::NT) {
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        reinterpret_cast<u32x4_t*>(K0)[x] = z;
+        reinterpret_cast<u32x4_t*>(V0)[x] = z;
+        reinterpret_cast<u32x4_t*>(K1)[x] = z;
+        reinterpret_cast<u32x4_t*>(V1)[x] = z;
+    }
+    __syncthreads();  // the zeros land before any tile load is issued
 
     int dense_item = -1;
     if (DENSE) {
@@ -183,7 +237,7 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             __syncthreads();
             if (tid == 0) misc_s[0] = claim_item(a.queues, H, NG);
             __syncthreads();
-            item = misc_s[0];
+            item = __builtin_amdgcn_readfirstlane(misc_s[0]);
             if (item < 0) break;
         }
         const int h = item / NG, gi = item % NG;
@@ -275,7 +329,7 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                 }
             }
             __syncthreads();
-            T = misc_s[1];
+            T = __builtin_amdgcn_readfirstlane(misc_s[1]);
         }
 
         // Q fragments (B operand of S^T = K Q^T): rows q0 + 32w + 16qt + l16
@@ -307,28 +361,32 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
         // entry of 64-key tile t: (approx?, part, row0 of the tile in its source)
         auto entry = [&](int t, bool& approx, uint32_t& part, int& row0) {
             const int e = t / S::SUB, sub = t % S::SUB;
-            const uint32_t d = DENSE ? ((all_part << kPartShift) | (uint32_t)e) : tiles[e];
+            // the entry is the same for the whole workgroup: keep it scalar
+            const uint32_t d = DENSE ? ((all_part << kPartShift) | (uint32_t)e)
+                                     : (uint32_t)__builtin_amdgcn_readfirstlane((int)tiles[e]);
             approx = (d & kApprox) != 0;
             part = (d >> kPartShift) & 3u;
             row0 = (int)(d & kIndexMask) * BLK + sub * 64;
         };
-        auto issue = [&](int t, u16* Kd, u16* Vd) {
+        auto source = [&](int t) {
             bool ap;
             uint32_t pt;
             int row0;
             entry(t, ap, pt, row0);
-            if (ap)
-                tile_issue<D, BLK>(a.kbar_bf + (size_t)h * N * D, a.vsum_bf + (size_t)h * N * D,
-                                   row0, N - 1, Kd, Vd, wave_s, tl);
-            else
-                tile_issue<D, BLK>(kg + head_off, vg + head_off, row0, L - 1, Kd, Vd, wave_s, tl);
+            // choose the source before forming its resources (kept scalar)
+            const u16* kp = ap ? a.kbar_bf + (size_t)h * N * D : kg + head_off;
+            const u16* vp = ap ? a.vsum_bf + (size_t)h * N * D : vg + head_off;
+            return tile_src<D>(kp, vp, row0, ap ? N : L);
+        };
+        auto issue = [&](int t, u16* Kd, u16* Vd) {
+            tile_issue<D, BLK>(source(t), Kd, Vd, wave_s, tl);
         };
 
         // compute tile t from (Kt, Vt) while tile t+1 streams into (Kn, Vn)
         auto step = [&](int t, const u16* Kt, const u16* Vt, u16* Kn, u16* Vn, int TS) {
             __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of tile t have landed
             __syncthreads();                // everyone's have; tile t-1 is no longer read
-            if (t + 1 < TS) issue(t + 1, Kn, Vn);
+            if (t + 1 < TS) issue(t + 1, Kn, Vn);  // tile t+1 streams into (Kn, Vn)
             bool approx;
             uint32_t part;
             int row0;
@@ -347,9 +405,7 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                 for (int sb = 0; sb < KB; ++sb)
 #pragma unroll
                     for (int kt = 0; kt < 4; ++kt) {
-                        const int r = kt * 16 + l16;
-                        kfr[sb][kt] = *reinterpret_cast<const u32x4_t*>(
-                            Kt + r * D + ((((s0 + sb) * 4 + g) ^ k_swz<D>(r)) << 3));
+                        kfr[sb][kt] = *reinterpret_cast<const u32x4_t*>(Kt + kt * 16 * D + koff_s[s0 + sb]);
                     }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -364,6 +420,7 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
+
 
             // column masks: tokens past L (exact), selected or past-N pooled
             // keys (approximate)
@@ -452,11 +509,8 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             // (e < 4) or 32u + 16 + 4g + (e - 4): the keys this lane holds.
             // The transposing read gives lane (l16, g) four keys of column
             // d = 16 dt + l16 from the row addresses of lanes 16g + p + 4e.
-            const int tp = l16 & 3, te = l16 >> 2;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-                const int key_lo = 32 * u + 4 * g + te;  // v_swz(key_lo + 16) == v_swz(key_lo)
-                const int vs = v_swz<D>(key_lo);
                 u32x4_t pb[2];
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt)
@@ -472,12 +526,11 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
 #pragma unroll
                     for (int db = 0; db < VB; ++db) {
                         const int dt = d0 + db;
-                        const int ch = (2 * dt + (tp >> 1)) ^ vs;
-                        const int off = ch * 8 + 4 * (tp & 1);
+                        // keys 32u + 4g + (l16 >> 2) and 16 further (same swizzle)
                         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4_t*)(Vt + key_lo * D + off));
+                            (lds_s16x4_t*)(Vt + 32 * u * D + voff_d[dt]));
                         const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4_t*)(Vt + (key_lo + 16) * D + off));
+                            (lds_s16x4_t*)(Vt + (32 * u + 16) * D + voff_d[dt]));
                         vfr[db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     }
                     __builtin_amdgcn_sched_barrier(0);
