@@ -41,6 +41,7 @@ int check_tensors(const void* q, const void* k, const void* v, const void* out, 
 //   tau              : fp32 [H][N]        thresholds
 //   queues           : int32[8]           sweep work counters
 //   kbar_bf, vsum_bf : bf16 [H][N][d]     MFMA operands of the approximate path
+//   sel              : u32  [H][N][W]     selection bits, W = ceil(N / 32)
 struct Workspace {
     float* qbar;
     float* kbar;
@@ -49,6 +50,7 @@ struct Workspace {
     int* queues;
     uint16_t* kbar_bf;
     uint16_t* vsum_bf;
+    uint32_t* sel;
     size_t bytes;
 };
 
@@ -58,6 +60,7 @@ Workspace carve(void* base, int H, int L, int d, int B) {
     const size_t pooled_bf = align_up(sizeof(uint16_t) * (size_t)H * N * d);
     const size_t taub = align_up(sizeof(float) * (size_t)H * N);
     const size_t qb = align_up(sizeof(int) * 8);
+    const size_t selb = align_up(sizeof(uint32_t) * (size_t)H * N * ((N + 31) / 32));
     char* p = static_cast<char*>(base);
     Workspace w;
     size_t off = 0;
@@ -68,6 +71,7 @@ Workspace carve(void* base, int H, int L, int d, int B) {
     w.queues = reinterpret_cast<int*>(p + off); off += qb;
     w.kbar_bf = reinterpret_cast<uint16_t*>(p + off); off += pooled_bf;
     w.vsum_bf = reinterpret_cast<uint16_t*>(p + off); off += pooled_bf;
+    w.sel = reinterpret_cast<uint32_t*>(p + off); off += selb;
     w.bytes = off;
     return w;
 }
@@ -79,14 +83,15 @@ hipError_t launch_sweep(const sol::AttnArgs& a, int bf16, int d, int B, bool den
 sol::AttnArgs sweep_args(const void* q, const void* k, const void* v, const float* qbar,
                          const float* kbar, const float* vsum, const float* tau,
                          const uint16_t* kbar_bf, const uint16_t* vsum_bf, int H, int L, int d,
-                         int B, void* out, int* counters, uint32_t* sel_mask) {
+                         int B, void* out, int* counters, const uint32_t* sel) {
     const int N = (L + B - 1) / B;
     sol::AttnArgs a = {};
     a.q = q; a.k = k; a.v = v;
     a.qbar = qbar; a.kbar = kbar; a.vsum = vsum; a.tau = tau;
     a.kbar_bf = kbar_bf; a.vsum_bf = vsum_bf;
     a.out = out;
-    a.sel_dbg = sel_mask;
+    a.sel = sel;
+    a.sel_dbg = nullptr;
     a.queues = counters;
     a.H = H; a.L = L; a.N = N; a.W = (N + 31) / 32;
     a.nlast = L - (N - 1) * B;
@@ -112,16 +117,19 @@ int forward(const void* q, const void* k, const void* v, int H, int L, int d, in
     const int N = (L + B - 1) / B;
     const int bf16 = dt == SOL_BF16;
     const float c = static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
-    // The thresholds go straight to the caller's array when it asks for them.
+    // The thresholds and selection bits go straight to the caller's arrays
+    // when it asks for them.
     float* tau = tau_out ? tau_out : w.tau;
+    uint32_t* sel = sel_mask ? sel_mask : w.sel;
 
     if (sol::launch_pool(q, k, v, bf16, H, L, d, B, w.qbar, w.kbar, w.vsum,
                          bf16 ? w.kbar_bf : nullptr, bf16 ? w.vsum_bf : nullptr, s) != hipSuccess)
         return SOL_EHIP;
-    if (sol::launch_route(w.qbar, w.kbar, H, N, d, c, beta, tau, kept, w.queues, s) != hipSuccess)
+    if (sol::launch_route(w.qbar, w.kbar, H, N, d, c, beta, nullptr, tau, kept, sel, w.queues, s) !=
+        hipSuccess)
         return SOL_EHIP;
     const sol::AttnArgs a = sweep_args(q, k, v, w.qbar, w.kbar, w.vsum, tau, w.kbar_bf, w.vsum_bf,
-                                       H, L, d, B, out, w.queues, sel_mask);
+                                       H, L, d, B, out, w.queues, sel);
     if (launch_sweep(a, bf16, d, B, false, s) != hipSuccess) return SOL_EHIP;
     return SOL_OK;
 }
@@ -159,7 +167,7 @@ int sol_route(const float* qbar, const float* kbar, int H, int L, int d, int B, 
         return SOL_EINVAL;
     const int N = (L + B - 1) / B;
     const float c = static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
-    if (sol::launch_route(qbar, kbar, H, N, d, c, beta, tau, kept_counts, nullptr,
+    if (sol::launch_route(qbar, kbar, H, N, d, c, beta, nullptr, tau, kept_counts, nullptr, nullptr,
                           static_cast<hipStream_t>(stream)) != hipSuccess)
         return SOL_EHIP;
     return SOL_OK;
@@ -190,8 +198,14 @@ int sol_sweep(const void* q, const void* k, const void* v, const float* qbar, co
     } else if (sol::launch_reset_counters(w.queues, s) != hipSuccess) {
         return SOL_EHIP;
     }
+    // selection bits against the caller's thresholds
+    uint32_t* sel = sel_mask ? sel_mask : w.sel;
+    const float c = static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
+    if (sol::launch_route(qbar, kbar, H, N, d, c, 0.0f, tau, nullptr, nullptr, sel, nullptr, s) !=
+        hipSuccess)
+        return SOL_EHIP;
     const sol::AttnArgs a = sweep_args(q, k, v, qbar, kbar, vsum, tau, w.kbar_bf, w.vsum_bf, H, L,
-                                       d, B, out, w.queues, sel_mask);
+                                       d, B, out, w.queues, sel);
     if (launch_sweep(a, bf16, d, B, false, s) != hipSuccess) return SOL_EHIP;
     return SOL_OK;
 }

@@ -79,7 +79,7 @@ __device__ __forceinline__ float wave_sum_xor16_32(float x) {
 // Eq. (11) right-hand side), computed by four consecutive lanes: lane quarter
 // qq sums d/4 products in index order with fused multiply-adds, then the
 // quarters are combined as (p0 + p1) + (p2 + p3).  The routing kernel and the
-// attention kernel both call exactly these two functions with the same
+// fp32 attention kernel both call exactly these two functions with the same
 // operands, so both see bit-identical scores and take identical decisions.
 // ---------------------------------------------------------------------------
 template <int D>

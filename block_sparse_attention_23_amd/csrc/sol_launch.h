@@ -17,7 +17,8 @@ struct AttnArgs {
     const uint16_t* kbar_bf;  // [H][N][d] bf16 copy of kbar (bf16 sweep, approximate path)
     const uint16_t* vsum_bf;  // [H][N][d] bf16 copy of vsum
     void* out;
-    uint32_t* sel_dbg;   // [H][N][W] or null
+    const uint32_t* sel; // [H][N][W] selection bits of the routing kernel (bf16 sweep)
+    uint32_t* sel_dbg;   // [H][N][W] or null (fp32 path: written by the sweep)
     int* queues;         // 8 per-XCD work counters (sol only)
     int H, L, N, W;
     int nlast;           // valid tokens in the last block
@@ -31,8 +32,11 @@ hipError_t launch_pool(const void* q, const void* k, const void* v, int bf16, in
                        uint16_t* vsum_bf, hipStream_t s);
 hipError_t launch_pooled_to_bf16(const float* kbar, const float* vsum, size_t n, uint16_t* kbar_bf,
                                  uint16_t* vsum_bf, int* queues, hipStream_t s);
+// Proxy rows, thresholds (computed, or taken from tau_in when it is not
+// null), kept counts and selection bits (when sel is not null).
 hipError_t launch_route(const float* qbar, const float* kbar, int H, int N, int d, float c,
-                        float beta, float* tau, int32_t* kept, int* queues, hipStream_t s);
+                        float beta, const float* tau_in, float* tau, int32_t* kept, uint32_t* sel,
+                        int* queues, hipStream_t s);
 hipError_t launch_sweep_bf16(const AttnArgs& a, int d, int B, bool dense, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int d, int B, bool dense, hipStream_t s);
 hipError_t launch_reset_counters(int* queues, hipStream_t s);

@@ -137,8 +137,10 @@ template <int D, int R>
 __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qbar,
                                                     const float* __restrict__ kbar, int N,
                                                     int groups_per_head, float c, float beta,
+                                                    const float* __restrict__ tau_in,
                                                     float* __restrict__ tau_out,
                                                     int32_t* __restrict__ kept,
+                                                    uint32_t* __restrict__ sel, int W,
                                                     int* __restrict__ queues) {
     extern __shared__ float rows[];  // [R][N]
     __shared__ float qb[R][QbarLds<D>::SIZE];
@@ -184,13 +186,21 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
         for (int off = 32; off >= 1; off >>= 1) pv += __shfl_xor(pv, off);
         const float sigma = sqrtf(fmaxf(pv / static_cast<float>(N), 0.0f));
         float tau;
-        if (isinf(beta)) tau = beta;  // -inf: every block exact; +inf: none
+        if (tau_in) tau = tau_in[(size_t)h * N + i0 + r];  // thresholds given by the caller
+        else if (isinf(beta)) tau = beta;                  // -inf: every block exact; +inf: none
         else tau = __builtin_fmaf(beta, sigma, mu);
+        // selection bits of the row, 64 blocks per ballot (bit j % 32 of
+        // word j / 32 is block j), and their count
+        uint32_t* srow = sel ? sel + ((size_t)h * N + i0 + r) * W : nullptr;
         int cnt = 0;
-        for (int j = lane; j < N; j += 64) cnt += row[j] > tau ? 1 : 0;
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
-        if (lane == 0) {
+        for (int j0 = 0; j0 < N; j0 += 64) {
+            const int j = j0 + lane;
+            const uint64_t m = __ballot(j < N && row[j] > tau);
+            cnt += __popcll(m);
+            const int w0 = j0 >> 5;
+            if (srow && lane < 2 && w0 + lane < W) srow[w0 + lane] = static_cast<uint32_t>(m >> (32 * lane));
+        }
+        if (lane == 0 && !tau_in) {
             tau_out[(size_t)h * N + i0 + r] = tau;
             kept[(size_t)h * N + i0 + r] = cnt;
         }
@@ -219,24 +229,28 @@ hipError_t pool_t(const void* q, const void* k, const void* v, int bf16, int H, 
 
 template <int D, int R>
 hipError_t route_t(const float* qbar, const float* kbar, int H, int N, float c, float beta,
-                   float* tau, int32_t* kept, int* queues, hipStream_t s) {
+                   const float* tau_in, float* tau, int32_t* kept, uint32_t* sel, int* queues,
+                   hipStream_t s) {
     const int gph = (N + R - 1) / R;
     const size_t shm = sizeof(float) * (size_t)R * N;
     hipLaunchKernelGGL((route_kernel<D, R>), dim3(H * gph), dim3(256), shm, s, qbar, kbar, N, gph, c,
-                       beta, tau, kept, queues);
+                       beta, tau_in, tau, kept, sel, (N + 31) / 32, queues);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t route_d(const float* qbar, const float* kbar, int H, int N, float c, float beta,
-                   float* tau, int32_t* kept, int* queues, hipStream_t s) {
+                   const float* tau_in, float* tau, int32_t* kept, uint32_t* sel, int* queues,
+                   hipStream_t s) {
     // as many rows per workgroup as 64 KB of LDS holds
     const size_t row_bytes = sizeof(float) * ((size_t)N + QbarLds<D>::SIZE);
-    if (16 * row_bytes <= 65536) return route_t<D, 16>(qbar, kbar, H, N, c, beta, tau, kept, queues, s);
-    if (8 * row_bytes <= 65536) return route_t<D, 8>(qbar, kbar, H, N, c, beta, tau, kept, queues, s);
-    if (4 * row_bytes <= 65536) return route_t<D, 4>(qbar, kbar, H, N, c, beta, tau, kept, queues, s);
-    if (2 * row_bytes <= 65536) return route_t<D, 2>(qbar, kbar, H, N, c, beta, tau, kept, queues, s);
-    return route_t<D, 1>(qbar, kbar, H, N, c, beta, tau, kept, queues, s);
+#define SOL_ROUTE(R) route_t<D, R>(qbar, kbar, H, N, c, beta, tau_in, tau, kept, sel, queues, s)
+    if (16 * row_bytes <= 65536) return SOL_ROUTE(16);
+    if (8 * row_bytes <= 65536) return SOL_ROUTE(8);
+    if (4 * row_bytes <= 65536) return SOL_ROUTE(4);
+    if (2 * row_bytes <= 65536) return SOL_ROUTE(2);
+    return SOL_ROUTE(1);
+#undef SOL_ROUTE
 }
 
 }  // namespace
@@ -267,9 +281,10 @@ hipError_t launch_reset_counters(int* queues, hipStream_t s) {
 }
 
 hipError_t launch_route(const float* qbar, const float* kbar, int H, int N, int d, float c,
-                        float beta, float* tau, int32_t* kept, int* queues, hipStream_t s) {
-    if (d == 64) return route_d<64>(qbar, kbar, H, N, c, beta, tau, kept, queues, s);
-    if (d == 128) return route_d<128>(qbar, kbar, H, N, c, beta, tau, kept, queues, s);
+                        float beta, const float* tau_in, float* tau, int32_t* kept, uint32_t* sel,
+                        int* queues, hipStream_t s) {
+    if (d == 64) return route_d<64>(qbar, kbar, H, N, c, beta, tau_in, tau, kept, sel, queues, s);
+    if (d == 128) return route_d<128>(qbar, kbar, H, N, c, beta, tau_in, tau, kept, sel, queues, s);
     return hipErrorInvalidValue;
 }
 

@@ -6,14 +6,13 @@
 //
 // Per workgroup ("Sol-Attn" visual explainer, "The complete idea in one
 // pass", Eq. (4), Eq. (9), Eq. (10), Eq. (11)):
-//   1. routing on chip: the proxy scores s_ij of every pooled key are
-//      recomputed with the routing kernel's own arithmetic and compared with
-//      tau_i of each query block, giving one N-bit decision mask per block in
-//      LDS.  Scores are never written to memory.  A tile list follows: one
-//      approximate entry per chunk of B pooled keys that holds an unselected
-//      block of either query block, then one exact entry per key block that
-//      either query block selected (the union, so a key block chosen by both
-//      is loaded once), each tagged with the query blocks that use it.
+//   1. the tile list: the routing kernel's selection bits of the two query
+//      blocks (bit j of block i is s_ij > tau_i) are copied to LDS; a tile
+//      list follows: one approximate entry per chunk of B pooled keys that
+//      holds an unselected block of either query block, then one exact entry
+//      per key block that either query block selected (the union, so a key
+//      block chosen by both is loaded once), each tagged with the query
+//      blocks that use it.
 //   2. the tile loop over 64-key tiles.  Tiles stream from HBM straight into
 //      LDS (global_load_lds, 16 bytes a lane) into two buffers, so the next
 //      tile loads while the current one is computed; K and V stay row-major
@@ -169,8 +168,6 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
     __shared__ __align__(16) u16 V0[S::TILE];
     __shared__ __align__(16) u16 K1[S::TILE];
     __shared__ __align__(16) u16 V1[S::TILE];
-    __shared__ __align__(16) float qb_s[S::QB][QbarLds<D>::SIZE];
-    __shared__ float tau_s[S::QB];
     __shared__ int misc_s[2];
     extern __shared__ __align__(16) uint32_t dyn[];  // selection bits per block, then tile list
 
@@ -250,31 +247,12 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
         if (DENSE) {
             T = N;
         } else {
-            // ---- 1. routing on chip --------------------------------------
-            for (int t = tid; t < S::QB * D; t += S::NT) {
-                const int b = t / D, x = t % D;
-                qb_s[b][QbarLds<D>::index(x)] = b < nqb ? a.qbar[((size_t)h * N + i0 + b) * D + x] : 0.0f;
-            }
-            if (tid < S::QB) tau_s[tid] = tid < nqb ? a.tau[(size_t)h * N + i0 + tid] : INFINITY;
-            __syncthreads();
-            {
-                const int jj = tid >> 2, qq = tid & 3;
-                const size_t kb_head = (size_t)h * N * D;
-                for (int j0 = 0; j0 < N; j0 += 64) {
-                    const int j = j0 + jj;
-                    float kv[D / 4];
-                    load_kbar_quarter<D>(a.kbar + kb_head + (size_t)min(j, N - 1) * D, qq, kv);
-#pragma unroll
-                    for (int b = 0; b < S::QB; ++b) {
-                        const float s = proxy_from_quarter<D>(qb_s[b], kv, qq, a.c);
-                        const bool sel = j < N && s > tau_s[b];
-                        const uint32_t bits = every_fourth_bit(__ballot(sel));
-                        const int kb = j0 + wave * 16;
-                        if (lane == 0 && kb < N)
-                            reinterpret_cast<uint16_t*>(selbits + b * nwords)[kb >> 4] =
-                                static_cast<uint16_t>(bits);
-                    }
-                }
+            // ---- 1. the tile list ------------------------------------------
+            // selection bits of the group's query blocks (written by the
+            // routing kernel: bit j of block i is s_ij > tau_i)
+            for (int t = tid; t < S::QB * nwords; t += S::NT) {
+                const int b = t / nwords, w = t % nwords;
+                selbits[t] = b < nqb ? a.sel[((size_t)h * N + i0 + b) * a.W + w] : 0u;
             }
             __syncthreads();
             if (wave == 0) {
@@ -316,17 +294,6 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                     nt += __popcll(m);
                 }
                 if (lane == 0) misc_s[1] = nt;
-                if (a.sel_dbg) {
-                    for (int b = 0; b < nqb; ++b) {
-                        uint32_t* dst = a.sel_dbg + ((size_t)h * N + i0 + b) * a.W;
-                        for (int w = lane; w < nwords; w += 64) {
-                            uint32_t wd = selbits[b * nwords + w];
-                            const int valid = N - 32 * w;
-                            if (valid < 32) wd &= (1u << valid) - 1u;
-                            dst[w] = wd;
-                        }
-                    }
-                }
             }
             __syncthreads();
             T = __builtin_amdgcn_readfirstlane(misc_s[1]);
