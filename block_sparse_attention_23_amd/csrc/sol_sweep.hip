@@ -57,22 +57,25 @@ struct Sweep {
     static constexpr int NS = D / 32;                   // 32-deep steps over d
     static constexpr int NDT = D / 16;                  // 16-wide d tiles of O^T
     static constexpr int TILE = 64 * D;                 // elements of a K (or V) tile
+    // LDS layout of the K (or V) rows of a tile: NB blocks of 1 KB plus
+    // padding; key k is row k / NB of block k % NB.
+    static constexpr int NB = 64 * 2 * D / 1024;        // blocks per tile half
+    static constexpr int KPAD = 8, VPAD = 16;            // padding per block (elements)
+    static constexpr int KSLOT = NB * (512 + KPAD);      // elements of a K buffer
+    static constexpr int VSLOT = NB * (512 + VPAD);      // elements of a V buffer
 };
 
 constexpr uint32_t kApprox = 0x80000000u;  // tile-list entry: approximate chunk
 constexpr int kPartShift = 29;             // bits 29..30: query blocks using the entry
 constexpr uint32_t kIndexMask = (1u << kPartShift) - 1u;
 
-// LDS swizzles (the 16-byte chunk c of tile row r is stored at c ^ swz(r)),
-// chosen by measuring SQ_LDS_BANK_CONFLICT on gfx950: a b128 read serves 16
-// lanes per cycle, the transposing b64 read 32, over 64 four-byte banks.
-// K rows: the 16 rows read together must cover 16 distinct 16-byte slots.
-// V rows: the 8 key rows x 4 column chunks read together by the transposing
-// read must cover 32 distinct 8-byte slots.
-template <int D>
-__device__ __forceinline__ int k_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-template <int D>
-__device__ __forceinline__ int v_swz(int r) { return D == 128 ? ((r & 7) << 1) : (((r >> 1) & 3) << 1); }
+// LDS layout of the K rows (or V rows) of a tile, chosen so that the reads
+// below are free of bank conflicts on gfx950 (a 16-byte read serves 16 lanes
+// per cycle, the transposing 8-byte read 32, over 64 four-byte banks) and
+// every part of a read address other than the lane's own offset is an
+// instruction immediate: key k sits in row k / NB of 1 KB block k % NB, and
+// the blocks are padded by 16 bytes (K) or 32 bytes (V), so the 16 keys of a
+// K read, or the 8 keys of a transposing V read, start in different banks.
 
 // Keep bits 0, 4, 8, ..., 60 of m and pack them into bits 0..15.
 __device__ __forceinline__ uint32_t every_fourth_bit(uint64_t m) {
@@ -84,26 +87,15 @@ __device__ __forceinline__ uint32_t every_fourth_bit(uint64_t m) {
     return static_cast<uint32_t>(x);
 }
 
-// Per-lane byte offsets of the direct-to-LDS loads of a 64-row tile, fixed
-// for the kernel: load i of this lane fetches tile row
-// r = (wave*LPT + i)*RPK + lane/CH, 16-byte chunk (lane % CH) ^ swz(r), into
-// 1 KB LDS block wave*LPT + i (lane l writes bytes 16 l .. 16 l + 15).
+// Direct-to-LDS loads of a tile: load i of wave w fills block b = w*LPT + i
+// of the K (and of the V) buffer -- lane l writes bytes 16 l .. 16 l + 15 of
+// it, i.e. row l / CH of the block, 16-byte chunk l % CH, which holds key
+// (l / CH) * NB + b.  Its source offset is the lane's offset for load 0 plus
+// 2 D i bytes.
 template <int D, int BLK>
-struct TileLanes {
-    uint32_t koff[Sweep<D, BLK>::LPT];
-    uint32_t voff[Sweep<D, BLK>::LPT];
-};
-
-template <int D, int BLK>
-__device__ __forceinline__ void tile_lanes_init(TileLanes<D, BLK>& tl, int wave, int lane) {
+__device__ __forceinline__ uint32_t dma_lane_base(int wave, int lane) {
     using S = Sweep<D, BLK>;
-#pragma unroll
-    for (int i = 0; i < S::LPT; ++i) {
-        const int r = (wave * S::LPT + i) * S::RPK + lane / S::CH;
-        const int ph = lane % S::CH;
-        tl.koff[i] = (uint32_t)(2 * (r * D + ((ph ^ k_swz<D>(r)) << 3)));
-        tl.voff[i] = (uint32_t)(2 * (r * D + ((ph ^ v_swz<D>(r)) << 3)));
-    }
+    return (uint32_t)(((lane / S::CH) * S::NB + wave * S::LPT) * 2 * D + 16 * (lane % S::CH));
 }
 
 // Buffer resources of one 64-row tile: rows row0 .. row0+63 of a source with
@@ -144,18 +136,21 @@ __device__ __forceinline__ TileSrc tile_src(const u16* kp, const u16* vp, int ro
 }
 
 // Issue this wave's LPT pairs of direct-to-LDS loads (one K, one V) of a
-// tile.  wave_s is the wave index in an SGPR.
-template <int D, int BLK>
+// tile, load I and then the rest.  The source step goes into the lane offset
+// (an instruction offset would move the LDS destination as well).  wave_s is
+// the wave index in an SGPR.
+template <int D, int BLK, int I = 0>
 __device__ __forceinline__ void tile_issue(const TileSrc& src, u16* Kdst, u16* Vdst, int wave_s,
-                                           const TileLanes<D, BLK>& tl) {
+                                           uint32_t lane_base) {
     using S = Sweep<D, BLK>;
-#pragma unroll
-    for (int i = 0; i < S::LPT; ++i) {
+    if constexpr (I < S::LPT) {
 #if defined(__HIP_DEVICE_COMPILE__)
-        const int blk = (wave_s * S::LPT + i) * 512;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, (lds_void_t*)(Kdst + blk), 16, tl.koff[i], 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void_t*)(Vdst + blk), 16, tl.voff[i], 0, 0, 0);
+        const int b = wave_s * S::LPT + I;
+        const uint32_t off = lane_base + 2u * D * I;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, (lds_void_t*)(Kdst + b * (512 + S::KPAD)), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void_t*)(Vdst + b * (512 + S::VPAD)), 16, off, 0, 0, 0);
 #endif
+        tile_issue<D, BLK, I + 1>(src, Kdst, Vdst, wave_s, lane_base);
     }
 }
 
@@ -164,10 +159,10 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
     using S = Sweep<D, BLK>;
     // two tile buffers as four distinct objects, so the compiler can tell
     // that the loads landing in one buffer do not alias reads of the other
-    __shared__ __align__(16) u16 K0[S::TILE];
-    __shared__ __align__(16) u16 V0[S::TILE];
-    __shared__ __align__(16) u16 K1[S::TILE];
-    __shared__ __align__(16) u16 V1[S::TILE];
+    __shared__ __align__(16) u16 K0[S::KSLOT];
+    __shared__ __align__(16) u16 V0[S::VSLOT];
+    __shared__ __align__(16) u16 K1[S::KSLOT];
+    __shared__ __align__(16) u16 V1[S::VSLOT];
     __shared__ int misc_s[2];
     extern __shared__ __align__(16) uint32_t dyn[];  // selection bits per block, then tile list
 
@@ -186,33 +181,28 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
     uint32_t* tiles = dyn + S::QB * nwords;  // up to NC + N entries
     const int myb = (wave * 32) / BLK;       // this wave's query block within the group
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-    TileLanes<D, BLK> tl;
-    tile_lanes_init<D, BLK>(tl, wave, lane);
-    // per-lane LDS read offsets (elements), fixed for the kernel; the other
-    // parts of each read address (16-key tile, 32-key step, buffer) are
-    // compile-time constants.  K: 16-byte chunk 4s+g of key row l16 for
-    // 32-deep step s.  V: the transposing read of d tile dt for key row
-    // 4g + (l16 >> 2), column chunk 2dt + ((l16 & 3) >> 1), 8-byte half l16 & 1.
-    uint32_t koff_s[S::NS], voff_d[S::NDT];
-#pragma unroll
-    for (int s = 0; s < S::NS; ++s) koff_s[s] = (uint32_t)(l16 * D + (((s * 4 + g) ^ k_swz<D>(l16)) << 3));
-    {
-        const int tp = l16 & 3, key = 4 * g + (l16 >> 2);
-        const int vs = v_swz<D>(key);
-#pragma unroll
-        for (int dt = 0; dt < S::NDT; ++dt)
-            voff_d[dt] = (uint32_t)(key * D + (((2 * dt + (tp >> 1)) ^ vs) << 3) + 4 * (tp & 1));
-    }
+    const uint32_t dma_base = dma_lane_base<D, BLK>(wave_s, lane);
+    // per-lane LDS read offsets (elements); the rest of each read address
+    // (16-key tile, 32-deep or 32-key step, d tile, buffer) is an immediate.
+    // K: key l16 of a 16-key tile, 16-byte chunk g of a 32-deep step.  V: the
+    // transposing read of key 4g + (l16 >> 2) of a 16-key group, columns
+    // 8 ((l16 & 3) >> 1) + 4 (l16 & 1) of a 16-wide d tile.
+    const int k_lane = (l16 % S::NB) * (512 + S::KPAD) + (l16 / S::NB) * D + 8 * g;
+    const int k4 = 4 * g + (l16 >> 2), tp = l16 & 3;
+    const int v_lane = (k4 % S::NB) * (512 + S::VPAD) + (k4 / S::NB) * D + 8 * (tp >> 1) + 4 * (tp & 1);
 
     // The tile buffers start zeroed: a direct-to-LDS load of a row past the
     // end of its source is dropped by the buffer range check, so such rows
     // hold zeros or rows of an earlier tile -- finite values in masked
     // columns, whose weights are exactly zero.
-    for (int x = tid; x < S::TILE / 8; x += S::NT) {
+    for (int x = tid; x < S::KSLOT / 8; x += S::NT) {
         const u32x4_t z = {0u, 0u, 0u, 0u};
         reinterpret_cast<u32x4_t*>(K0)[x] = z;
-        reinterpret_cast<u32x4_t*>(V0)[x] = z;
         reinterpret_cast<u32x4_t*>(K1)[x] = z;
+    }
+    for (int x = tid; x < S::VSLOT / 8; x += S::NT) {
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+        reinterpret_cast<u32x4_t*>(V0)[x] = z;
         reinterpret_cast<u32x4_t*>(V1)[x] = z;
     }
     __syncthreads();  // the zeros land before any tile load is issued
@@ -346,19 +336,19 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             return tile_src<D>(kp, vp, row0, ap ? N : L);
         };
         auto issue = [&](int t, u16* Kd, u16* Vd) {
-            tile_issue<D, BLK>(source(t), Kd, Vd, wave_s, tl);
+            tile_issue<D, BLK>(source(t), Kd, Vd, wave_s, dma_base);
         };
 
         // compute tile t from (Kt, Vt) while tile t+1 streams into (Kn, Vn)
         auto step = [&](int t, const u16* Kt, const u16* Vt, u16* Kn, u16* Vn, int TS) {
             __builtin_amdgcn_s_waitcnt(0);  // this thread's loads of tile t have landed
             __syncthreads();                // everyone's have; tile t-1 is no longer read
-            if (t + 1 < TS) issue(t + 1, Kn, Vn);  // tile t+1 streams into (Kn, Vn)
             bool approx;
             uint32_t part;
             int row0;
             entry(t, approx, part, row0);
-            if (!((part >> myb) & 1u)) return;  // this wave's query block does not use it
+            if (t + 1 < TS) issue(t + 1, Kn, Vn);  // tile t+1 streams into (Kn, Vn)
+            if (!((part >> myb) & 1u)) return;    // this wave's query block does not use it
 
             // S^T = K Q^T for this wave's 32 query rows, in batches of KB
             // k-steps: the batch's K fragments are read first (LDS reads in
@@ -372,7 +362,8 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                 for (int sb = 0; sb < KB; ++sb)
 #pragma unroll
                     for (int kt = 0; kt < 4; ++kt) {
-                        kfr[sb][kt] = *reinterpret_cast<const u32x4_t*>(Kt + kt * 16 * D + koff_s[s0 + sb]);
+                        kfr[sb][kt] = *reinterpret_cast<const u32x4_t*>(
+                            Kt + k_lane + kt * (16 / S::NB) * D + 32 * (s0 + sb));
                     }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -390,21 +381,26 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
 
 
             // column masks: tokens past L (exact), selected or past-N pooled
-            // keys (approximate)
+            // keys (approximate).  Lane key jj = 16 kt + 4g + r is bit
+            // 16 kt + r of colsel >> 4g.
             const int limit = approx ? N : L;
-            uint64_t colsel = 0;
-            if (approx) {
-                const uint32_t* sb = selbits + myb * nwords;
-                if (row0 < N) colsel = sb[row0 >> 5];
-                if (row0 + 32 < N) colsel |= static_cast<uint64_t>(sb[(row0 >> 5) + 1]) << 32;
-            }
             if (approx || row0 + 64 > limit) {
+                uint64_t colsel = 0;
+                if (approx) {
+                    const uint32_t* sb = selbits + myb * nwords;
+                    if (row0 < N) colsel = sb[row0 >> 5];
+                    if (row0 + 32 < N) colsel |= static_cast<uint64_t>(sb[(row0 >> 5) + 1]) << 32;
+                }
+                colsel >>= 4 * g;
+                const uint32_t cs_lo = (uint32_t)colsel, cs_hi = (uint32_t)(colsel >> 32);
+                const int lim = limit - row0, g4 = 4 * g;
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const int jj = kt * 16 + g * 4 + r;
-                        const bool valid = row0 + jj < limit && !((colsel >> jj) & 1ull);
+                        const int bit = kt * 16 + r;
+                        const uint32_t w = bit < 32 ? cs_lo : cs_hi;
+                        const bool valid = g4 < lim - bit && !((w >> (bit & 31)) & 1u);
                         if (!valid) sacc[kt][0][r] = sacc[kt][1][r] = -INFINITY;
                     }
             }
@@ -493,11 +489,11 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
 #pragma unroll
                     for (int db = 0; db < VB; ++db) {
                         const int dt = d0 + db;
-                        // keys 32u + 4g + (l16 >> 2) and 16 further (same swizzle)
+                        // keys 32u + 4g + (l16 >> 2) and 16 further
                         const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4_t*)(Vt + 32 * u * D + voff_d[dt]));
+                            (lds_s16x4_t*)(Vt + v_lane + (32 * u / S::NB) * D + 16 * dt));
                         const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4_t*)(Vt + (32 * u + 16) * D + voff_d[dt]));
+                            (lds_s16x4_t*)(Vt + v_lane + ((32 * u + 16) / S::NB) * D + 16 * dt));
                         vfr[db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     }
                     __builtin_amdgcn_sched_barrier(0);
