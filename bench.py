@@ -186,6 +186,7 @@ def main():
     qbar = torch.empty((H, N, d), dtype=torch.float32, device="cuda")
     kbar, vsum = torch.empty_like(qbar), torch.empty_like(qbar)
     tau = torch.empty((H, N), dtype=torch.float32, device="cuda")
+    bits = torch.empty((H, N, binding.sel_words(N)), dtype=torch.int32, device="cuda")
     beta0 = head["beta"]
     s = torch.cuda.current_stream()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
@@ -194,9 +195,9 @@ def main():
         if e: e[0].record(s)
         binding.pool(q, k, v, B, outs=(qbar, kbar, vsum))
         if e: e[1].record(s)
-        binding.route(qbar, kbar, L, B, beta0, tau=tau, kept=kept)
+        binding.route(qbar, kbar, L, B, beta0, tau=tau, kept=kept, sel_bits=bits)
         if e: e[2].record(s)
-        binding.sweep(q, k, v, qbar, kbar, vsum, tau, B, out=out, workspace=ws)
+        binding.sweep(q, k, v, qbar, kbar, vsum, tau, B, out=out, workspace=ws, sel_bits=bits)
         if e: e[3].record(s)
     torch.cuda.synchronize()
     st = {"pool": 0.0, "route": 0.0, "sweep": 0.0}

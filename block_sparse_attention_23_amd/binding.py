@@ -19,10 +19,9 @@ _FUNCS = {
     "sol_pool": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 5
                  + [ctypes.c_void_p] * 4),
     "sol_route": (ctypes.c_int, [ctypes.c_void_p] * 2 + [ctypes.c_int] * 4
-                  + [ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+                  + [ctypes.c_float] + [ctypes.c_void_p] * 4),
     "sol_sweep": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 5
-                  + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                     ctypes.c_void_p]),
+                  + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t] + [ctypes.c_void_p] * 3),
     "sol_attn_fwd": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4
                      + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
@@ -127,8 +126,9 @@ def pool(q, k, v, B, outs=None, stream=None):
     return tuple(outs)
 
 
-def route(qbar, kbar, L, B, beta, tau=None, kept=None, stream=None):
-    """Thresholds tau [H][N] and kept counts [H][N] from pooled tensors."""
+def route(qbar, kbar, L, B, beta, tau=None, kept=None, sel_bits=None, stream=None):
+    """Thresholds tau [H][N] and kept counts [H][N] from pooled tensors; with
+    sel_bits (int32 [H][N][ceil(N/32)]) also the decisions as bits."""
     H, N, d = qbar.shape
     if not (qbar.is_cuda and kbar.is_cuda):
         raise ValueError("pooled tensors must live on the GPU")
@@ -139,13 +139,20 @@ def route(qbar, kbar, L, B, beta, tau=None, kept=None, stream=None):
     with torch.cuda.device(qbar.device):
         _check("sol_route", lib().sol_route(qbar.data_ptr(), kbar.data_ptr(), H, L, d, B,
                                             float(beta), tau.data_ptr(), kept.data_ptr(),
+                                            None if sel_bits is None else sel_bits.data_ptr(),
                                             _stream_ptr(stream, qbar.device)))
     return tau, kept
 
 
-def sweep(q, k, v, qbar, kbar, vsum, tau, B, out=None, workspace=None, sel_mask=None,
-          stream=None):
-    """The fused exact/approximate sweep given pooled tensors and thresholds."""
+def sel_words(N):
+    """uint32 words per selection row."""
+    return (N + 31) // 32
+
+
+def sweep(q, k, v, qbar, kbar, vsum, tau, B, out=None, workspace=None, sel_bits=None,
+          sel_mask=None, stream=None):
+    """The fused exact/approximate sweep given pooled tensors and thresholds
+    (and, optionally, the decisions sol_route wrote for them)."""
     H, L, d = _tokens(q, k, v)
     if out is None:
         out = torch.empty_like(q)
@@ -156,6 +163,7 @@ def sweep(q, k, v, qbar, kbar, vsum, tau, B, out=None, workspace=None, sel_mask=
             q.data_ptr(), k.data_ptr(), v.data_ptr(), qbar.data_ptr(), kbar.data_ptr(),
             vsum.data_ptr(), tau.data_ptr(), H, L, d, B, _dtype_code(q), out.data_ptr(),
             workspace.data_ptr(), workspace.numel(),
+            None if sel_bits is None else sel_bits.data_ptr(),
             None if sel_mask is None else sel_mask.data_ptr(), _stream_ptr(stream, q.device)))
     return out
 

@@ -159,15 +159,16 @@ int sol_pool(const void* q, const void* k, const void* v, int H, int L, int d, i
 }
 
 int sol_route(const float* qbar, const float* kbar, int H, int L, int d, int B, float beta,
-              float* tau, int32_t* kept_counts, void* stream) {
+              float* tau, int32_t* kept_counts, uint32_t* sel_bits, void* stream) {
     int st = check_shape(H, L, d, B);
     if (st != SOL_OK) return st;
     if (!qbar || !kbar || !tau || !kept_counts || isnan(beta)) return SOL_EINVAL;
-    if (!aligned(qbar, 16) || !aligned(kbar, 16) || !aligned(tau, 4) || !aligned(kept_counts, 4))
+    if (!aligned(qbar, 16) || !aligned(kbar, 16) || !aligned(tau, 4) || !aligned(kept_counts, 4) ||
+        (sel_bits && !aligned(sel_bits, 4)))
         return SOL_EINVAL;
     const int N = (L + B - 1) / B;
     const float c = static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
-    if (sol::launch_route(qbar, kbar, H, N, d, c, beta, nullptr, tau, kept_counts, nullptr, nullptr,
+    if (sol::launch_route(qbar, kbar, H, N, d, c, beta, nullptr, tau, kept_counts, sel_bits, nullptr,
                           static_cast<hipStream_t>(stream)) != hipSuccess)
         return SOL_EHIP;
     return SOL_OK;
@@ -175,14 +176,15 @@ int sol_route(const float* qbar, const float* kbar, int H, int L, int d, int B, 
 
 int sol_sweep(const void* q, const void* k, const void* v, const float* qbar, const float* kbar,
               const float* vsum, const float* tau, int H, int L, int d, int B, sol_dtype_t dt,
-              void* out, void* workspace, size_t ws_bytes, uint32_t* sel_mask, void* stream) {
+              void* out, void* workspace, size_t ws_bytes, const uint32_t* sel_bits,
+              uint32_t* sel_mask, void* stream) {
     int st = check_shape(H, L, d, B);
     if (st != SOL_OK) return st;
     st = check_tensors(q, k, v, out, dt);
     if (st != SOL_OK) return st;
     if (!qbar || !kbar || !vsum || !tau) return SOL_EINVAL;
     if (!aligned(qbar, 16) || !aligned(kbar, 16) || !aligned(vsum, 16) || !aligned(tau, 4) ||
-        (sel_mask && !aligned(sel_mask, 4)))
+        (sel_mask && !aligned(sel_mask, 4)) || (sel_bits && !aligned(sel_bits, 4)))
         return SOL_EINVAL;
     if (!workspace || !aligned(workspace, kAlign)) return SOL_EWORKSPACE;
     const Workspace w = carve(workspace, H, L, d, B);
@@ -198,12 +200,22 @@ int sol_sweep(const void* q, const void* k, const void* v, const float* qbar, co
     } else if (sol::launch_reset_counters(w.queues, s) != hipSuccess) {
         return SOL_EHIP;
     }
-    // selection bits against the caller's thresholds
-    uint32_t* sel = sel_mask ? sel_mask : w.sel;
-    const float c = static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
-    if (sol::launch_route(qbar, kbar, H, N, d, c, 0.0f, tau, nullptr, nullptr, sel, nullptr, s) !=
-        hipSuccess)
+    // selection bits against the caller's thresholds: the caller's, or
+    // derived here (and copied to sel_mask when it asks for them)
+    const size_t nsel = (size_t)H * N * ((N + 31) / 32);
+    const uint32_t* sel = sel_bits;
+    if (sel_bits && sel_mask &&
+        hipMemcpyAsync(sel_mask, sel_bits, nsel * sizeof(uint32_t), hipMemcpyDeviceToDevice, s) !=
+            hipSuccess)
         return SOL_EHIP;
+    if (!sel) {
+        uint32_t* dst = sel_mask ? sel_mask : w.sel;
+        const float c = static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
+        if (sol::launch_route(qbar, kbar, H, N, d, c, 0.0f, tau, nullptr, nullptr, dst, nullptr, s) !=
+            hipSuccess)
+            return SOL_EHIP;
+        sel = dst;
+    }
     const sol::AttnArgs a = sweep_args(q, k, v, qbar, kbar, vsum, tau, w.kbar_bf, w.vsum_bf, H, L,
                                        d, B, out, w.queues, sel);
     if (launch_sweep(a, bf16, d, B, false, s) != hipSuccess) return SOL_EHIP;

@@ -76,29 +76,39 @@ int sol_pool(const void* q, const void* k, const void* v,
  * qbar, kbar : DEVICE fp32 [H][N][d] (as written by sol_pool).
  * tau        : DEVICE fp32 [H][N], written.
  * kept_counts: DEVICE int32 [H][N], written.
- * The counts equal those of the sweep: both stages compute each s_ij with
- * the same arithmetic.
+ * sel_bits   : DEVICE uint32 [H][N][ceil(N/32)], written, or NULL: the
+ *              decisions themselves, bit (j % 32) of word j / 32 of row (h, i)
+ *              set iff s_ij > tau_i (the layout of sol_attn_fwd_dbg's
+ *              sel_mask).  sol_sweep can take them instead of deriving them.
+ * The counts and bits are those the forward pass uses: every stage computes
+ * each s_ij with the same arithmetic.
  */
 int sol_route(const float* qbar, const float* kbar, int H, int L, int d, int B,
-              float beta, float* tau, int32_t* kept_counts, void* stream);
+              float beta, float* tau, int32_t* kept_counts, uint32_t* sel_bits,
+              void* stream);
 
 /*
- * The fused sweep alone: given the pooled tensors and thresholds, for every
- * (h, i) stream the pooled keys in chunks, recompute their proxy scores,
- * route each key block (s_ij > tau_i: exact; otherwise approximate) and merge
- * both paths into one online softmax ("Sol-Attn" visual explainer, Eq. (9),
- * Eq. (10), Eq. (11); abstract).  Output as sol_attn_fwd.
+ * The fused sweep alone: given the pooled tensors and thresholds, route each
+ * key block of every (h, i) (s_ij > tau_i: exact; otherwise approximate) and
+ * merge both paths into one online softmax ("Sol-Attn" visual explainer,
+ * Eq. (9), Eq. (10), Eq. (11); abstract).  Output as sol_attn_fwd.
  * qbar, kbar, vsum : DEVICE fp32 [H][N][d] as written by sol_pool.
  * tau       : DEVICE fp32 [H][N] as written by sol_route.
  * workspace : DEVICE, at least sol_workspace_bytes(H, L, d, B) bytes,
  *             256-byte aligned (scratch: work counters and bf16 copies of the
  *             pooled keys and summed values).
- * sel_mask  : as in sol_attn_fwd_dbg, or NULL.
+ * sel_bits  : DEVICE, the decisions sol_route wrote for these thresholds, or
+ *             NULL.  bf16: when given, the sweep takes its decisions from
+ *             them and launches no routing pass of its own; when NULL it first
+ *             derives them from tau.  fp32: ignored (the fp32 kernel decides
+ *             from tau itself, with the same arithmetic).
+ * sel_mask  : as in sol_attn_fwd_dbg (the decisions taken), or NULL.
  */
 int sol_sweep(const void* q, const void* k, const void* v,
               const float* qbar, const float* kbar, const float* vsum, const float* tau,
               int H, int L, int d, int B, sol_dtype_t dt, void* out,
-              void* workspace, size_t ws_bytes, uint32_t* sel_mask, void* stream);
+              void* workspace, size_t ws_bytes, const uint32_t* sel_bits,
+              uint32_t* sel_mask, void* stream);
 
 /*
  * Sol-Attn forward ("Sol-Attn" visual explainer: Eq. (4) selection rule,

@@ -94,10 +94,11 @@ def test_pool_and_dense_reject_bad_arguments(lib):
 
 
 def test_stage_entry_points_reject_bad_arguments(lib):
-    assert lib.sol_route(FAKE, None, 1, 100, 64, 64, 1.0, FAKE, FAKE, None) == -1
-    assert lib.sol_route(FAKE, FAKE, 1, 100, 64, 64, math.nan, FAKE, FAKE, None) == -1
-    assert lib.sol_route(FAKE, FAKE, 1, 100, 64, 16, 1.0, FAKE, FAKE, None) == -2
-    args = [FAKE] * 7 + [1, 100, 64, 64, 0, FAKE, FAKE_WS, 1 << 30, None, None]
+    assert lib.sol_route(FAKE, None, 1, 100, 64, 64, 1.0, FAKE, FAKE, None, None) == -1
+    assert lib.sol_route(FAKE, FAKE, 1, 100, 64, 64, math.nan, FAKE, FAKE, None, None) == -1
+    assert lib.sol_route(FAKE, FAKE, 1, 100, 64, 16, 1.0, FAKE, FAKE, None, None) == -2
+    assert lib.sol_route(FAKE, FAKE, 1, 100, 64, 64, 1.0, FAKE, FAKE, FAKE + 2, None) == -1
+    args = [FAKE] * 7 + [1, 100, 64, 64, 0, FAKE, FAKE_WS, 1 << 30, None, None, None]
     bad = list(args)
     bad[13] = None  # workspace
     assert lib.sol_sweep(*bad) == -3
@@ -110,6 +111,9 @@ def test_stage_entry_points_reject_bad_arguments(lib):
     bad = list(args)
     bad[9] = 96  # d
     assert lib.sol_sweep(*bad) == -2
+    bad = list(args)
+    bad[15] = FAKE + 2  # misaligned selection bits
+    assert lib.sol_sweep(*bad) == -1
 
 
 def test_binding_refuses_cpu_tensors(lib):

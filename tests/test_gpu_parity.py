@@ -140,3 +140,27 @@ def test_workspace_reuse_across_shapes():
     # selection is the oracle's here unless a flip occurs; judge loosely on the mean
     err = np.abs(o_small.float().cpu().numpy() - ref)
     assert err.mean() <= TOL["bf16"][1]
+
+
+@pytest.mark.parametrize("dtype,d,B,L", [("bf16", 128, 64, 1000), ("bf16", 64, 128, 700),
+                                         ("fp32", 64, 64, 500)])
+def test_stage_entry_points_equal_forward(dtype, d, B, L):
+    """sol_pool -> sol_route -> sol_sweep (with the route's selection bits, and
+    without them) launches the forward pass's own kernels: identical output,
+    thresholds, kept counts and decisions."""
+    inp = grid_inp(2, L, d, dtype, seed=11)
+    q, k, v = to_device(inp)
+    H, N = q.shape[0], -(-L // B)
+    out_f, kept_f, sel_f, tau_f = binding.attn_fwd(q, k, v, B, 1.0, debug=True)
+    qb, kb, vs = binding.pool(q, k, v, B)
+    bits = torch.full((H, N, binding.sel_words(N)), -1, dtype=torch.int32, device="cuda")
+    tau, kept = binding.route(qb, kb, L, B, 1.0, sel_bits=bits)
+    mask_a = torch.full_like(bits, -1)
+    mask_b = torch.full_like(bits, -1)
+    out_a = binding.sweep(q, k, v, qb, kb, vs, tau, B, sel_bits=bits, sel_mask=mask_a)
+    out_b = binding.sweep(q, k, v, qb, kb, vs, tau, B, sel_mask=mask_b)
+    torch.cuda.synchronize()
+    assert torch.equal(tau, tau_f) and torch.equal(kept, kept_f)
+    for m in (bits, mask_a, mask_b):
+        assert torch.equal(m, sel_f)
+    assert torch.equal(out_a, out_f) and torch.equal(out_b, out_f)
