@@ -50,12 +50,18 @@ def parse():
 
 
 def source_digest():
+    """Digest of the kernel sources' code: comments and whitespace are
+    dropped first, so a comment edit keeps recorded counters valid."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_sparse_attention_23_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            code = fh.read()
+        code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(f.encode() + b"\0" + " ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -14,9 +14,9 @@
 //      block chosen by both is loaded once), each tagged with the query
 //      blocks that use it.
 //   2. the tile loop over 64-key tiles.  Tiles stream from HBM straight into
-//      LDS (global_load_lds, 16 bytes a lane) into two buffers, so the next
-//      tile loads while the current one is computed; K and V stay row-major
-//      in LDS with an XOR swizzle of 16-byte chunks.  Scores are formed
+//      LDS (direct-to-LDS buffer loads, 16 bytes a lane) into two buffers, so
+//      the next tile loads while the current one is computed; K and V rows
+//      sit in padded 1 KB LDS blocks (layout below).  Scores are formed
 //      transposed, S^T = K Q^T (each lane: one query row per 16-row tile, 4
 //      keys per 16-key tile), and O^T += V^T P^T takes V^T through the
 //      transposing LDS read (ds_read_b64_tr_b16) and P^T from registers.
