@@ -139,18 +139,18 @@ __device__ __forceinline__ TileSrc tile_src(const u16* kp, const u16* vp, int ro
 // tile, load I and then the rest.  The source step goes into the lane offset
 // (an instruction offset would move the LDS destination as well).  wave_s is
 // the wave index in an SGPR.
-template <int D, int BLK, int I = 0>
+template <int D, int BLK, int I = 0, int IEND = Sweep<D, BLK>::LPT>
 __device__ __forceinline__ void tile_issue(const TileSrc& src, u16* Kdst, u16* Vdst, int wave_s,
                                            uint32_t lane_base) {
     using S = Sweep<D, BLK>;
-    if constexpr (I < S::LPT) {
+    if constexpr (I < IEND) {
 #if defined(__HIP_DEVICE_COMPILE__)
         const int b = wave_s * S::LPT + I;
         const uint32_t off = lane_base + 2u * D * I;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, (lds_void_t*)(Kdst + b * (512 + S::KPAD)), 16, off, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void_t*)(Vdst + b * (512 + S::VPAD)), 16, off, 0, 0, 0);
 #endif
-        tile_issue<D, BLK, I + 1>(src, Kdst, Vdst, wave_s, lane_base);
+        tile_issue<D, BLK, I + 1, IEND>(src, Kdst, Vdst, wave_s, lane_base);
     }
 }
 
@@ -182,6 +182,10 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
     const int myb = (wave * 32) / BLK;       // this wave's query block within the group
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t dma_base = dma_lane_base<D, BLK>(wave_s, lane);
+    // when only one query block uses a tile, the other block's two waves
+    // load the next tile alone: wave w covers the loads of waves 2 (w & 1)
+    // and 2 (w & 1) + 1
+    const uint32_t dma_base2 = dma_lane_base<D, BLK>(2 * (wave_s & 1), lane);
     // per-lane LDS read offsets (elements); the rest of each read address
     // (16-key tile, 32-deep or 32-key step, d tile, buffer) is an immediate.
     // K: key l16 of a 16-key tile, 16-byte chunk g of a 32-deep step.  V: the
@@ -315,29 +319,33 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
         const uint32_t blk2 = l16 == 0 ? pack_bf16x2(static_cast<float>(BLK), static_cast<float>(BLK)) : 0u;
 
         const uint32_t all_part = (1u << nqb) - 1u;
-        // entry of 64-key tile t: (approx?, part, row0 of the tile in its source)
-        auto entry = [&](int t, bool& approx, uint32_t& part, int& row0) {
-            const int e = t / S::SUB, sub = t % S::SUB;
-            // the entry is the same for the whole workgroup: keep it scalar
-            const uint32_t d = DENSE ? ((all_part << kPartShift) | (uint32_t)e)
-                                     : (uint32_t)__builtin_amdgcn_readfirstlane((int)tiles[e]);
+        // Tile-list word of 64-key tile t: the raw LDS value, then the word
+        // itself, the same for the whole workgroup (kept scalar).
+        auto word_raw = [&](int t) -> uint32_t { return DENSE ? 0u : tiles[t / S::SUB]; };
+        auto word_of = [&](int t, uint32_t raw) -> uint32_t {
+            return DENSE ? ((all_part << kPartShift) | (uint32_t)(t / S::SUB))
+                         : (uint32_t)__builtin_amdgcn_readfirstlane((int)raw);
+        };
+        // (approx?, part, row0 of the tile in its source) of tile t
+        auto decode = [&](uint32_t d, int t, bool& approx, uint32_t& part, int& row0) {
             approx = (d & kApprox) != 0;
             part = (d >> kPartShift) & 3u;
-            row0 = (int)(d & kIndexMask) * BLK + sub * 64;
+            row0 = (int)(d & kIndexMask) * BLK + (t % S::SUB) * 64;
         };
-        auto source = [&](int t) {
+        auto source_of = [&](uint32_t d, int t) {
             bool ap;
             uint32_t pt;
             int row0;
-            entry(t, ap, pt, row0);
+            decode(d, t, ap, pt, row0);
             // choose the source before forming its resources (kept scalar)
             const u16* kp = ap ? a.kbar_bf + (size_t)h * N * D : kg + head_off;
             const u16* vp = ap ? a.vsum_bf + (size_t)h * N * D : vg + head_off;
             return tile_src<D>(kp, vp, row0, ap ? N : L);
         };
-        auto issue = [&](int t, u16* Kd, u16* Vd) {
-            tile_issue<D, BLK>(source(t), Kd, Vd, wave_s, dma_base);
-        };
+        // Carried from step to step, so that a step issues its loads right
+        // after its barrier with no LDS read first: the words of tiles t and
+        // t+1 (scalars).
+        uint32_t w_t = 0, w_t1 = 0;
 
         // compute tile t from (Kt, Vt) while tile t+1 streams into (Kn, Vn)
         auto step = [&](int t, const u16* Kt, const u16* Vt, u16* Kn, u16* Vn, int TS) {
@@ -346,39 +354,47 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             bool approx;
             uint32_t part;
             int row0;
-            entry(t, approx, part, row0);
-            if (t + 1 < TS) issue(t + 1, Kn, Vn);  // tile t+1 streams into (Kn, Vn)
-            if (!((part >> myb) & 1u)) return;    // this wave's query block does not use it
+            decode(w_t, t, approx, part, row0);
+            const bool mine = (part >> myb) & 1u;  // this wave's query block uses tile t
+            if (t + 1 < TS) {  // tile t+1 streams into (Kn, Vn)
+                if (S::QB == 1 || part == 3u)
+                    tile_issue<D, BLK>(source_of(w_t1, t + 1), Kn, Vn, wave_s, dma_base);
+                else if (!mine)
+                    tile_issue<D, BLK, 0, 2 * S::LPT>(source_of(w_t1, t + 1), Kn, Vn, 2 * (wave_s & 1),
+                                                      dma_base2);
+            }
+            const uint32_t raw2 = t + 2 < TS ? word_raw(t + 2) : 0u;
+            // move the carried state on to tile t+1
+            auto advance = [&]() __attribute__((always_inline)) {
+                w_t = w_t1;
+                w_t1 = t + 2 < TS ? word_of(t + 2, raw2) : 0u;
+            };
+            advance();
+            if (!mine) return;  // this wave's query block does not use tile t
 
-            // S^T = K Q^T for this wave's 32 query rows, in batches of KB
-            // k-steps: the batch's K fragments are read first (LDS reads in
-            // flight together), then the MFMAs consume them.
-            constexpr int KB = S::NS >= 2 ? 2 : 1;
+            // S^T = K Q^T for this wave's 32 query rows, one 32-deep step at a
+            // time; the K fragments of step s+1 are read before the MFMAs of
+            // step s, so each batch of LDS reads hides behind MFMA work.
             f32x4_t sacc[4][2];
+            u32x4_t kfr[2][4];
+            auto kread = [&](int st, u32x4_t (&dst)[4]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int s0 = 0; s0 < S::NS; s0 += KB) {
-                u32x4_t kfr[KB][4];
+                for (int kt = 0; kt < 4; ++kt)
+                    dst[kt] = *reinterpret_cast<const u32x4_t*>(Kt + k_lane + kt * (16 / S::NB) * D + 32 * st);
+            };
+            kread(0, kfr[0]);
 #pragma unroll
-                for (int sb = 0; sb < KB; ++sb)
-#pragma unroll
-                    for (int kt = 0; kt < 4; ++kt) {
-                        kfr[sb][kt] = *reinterpret_cast<const u32x4_t*>(
-                            Kt + k_lane + kt * (16 / S::NB) * D + 32 * (s0 + sb));
-                    }
+            for (int st = 0; st < S::NS; ++st) {
+                if (st + 1 < S::NS) kread(st + 1, kfr[(st + 1) & 1]);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int sb = 0; sb < KB; ++sb) {
-#pragma unroll
-                    for (int kt = 0; kt < 4; ++kt) {
-                        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-                        const int s = s0 + sb;
-                        sacc[kt][0] = mfma16(as_bf16x8(kfr[sb][kt]), qf[0][s], s == 0 ? z : sacc[kt][0]);
-                        sacc[kt][1] = mfma16(as_bf16x8(kfr[sb][kt]), qf[1][s], s == 0 ? z : sacc[kt][1]);
-                    }
+                for (int kt = 0; kt < 4; ++kt) {
+                    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+                    sacc[kt][0] = mfma16(as_bf16x8(kfr[st & 1][kt]), qf[0][st], st == 0 ? z : sacc[kt][0]);
+                    sacc[kt][1] = mfma16(as_bf16x8(kfr[st & 1][kt]), qf[1][st], st == 0 ? z : sacc[kt][1]);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
-
 
             // column masks: tokens past L (exact), selected or past-N pooled
             // keys (approximate).  Lane key jj = 16 kt + 4g + r is bit
@@ -472,45 +488,58 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             // (e < 4) or 32u + 16 + 4g + (e - 4): the keys this lane holds.
             // The transposing read gives lane (l16, g) four keys of column
             // d = 16 dt + l16 from the row addresses of lanes 16g + p + 4e.
+            u32x4_t pb[2][2];
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                u32x4_t pb[2];
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int qt = 0; qt < 2; ++qt)
-                    pb[qt] = u32x4_t{pack_bf16x2(sacc[2 * u][qt][0], sacc[2 * u][qt][1]),
-                                     pack_bf16x2(sacc[2 * u][qt][2], sacc[2 * u][qt][3]),
-                                     pack_bf16x2(sacc[2 * u + 1][qt][0], sacc[2 * u + 1][qt][1]),
-                                     pack_bf16x2(sacc[2 * u + 1][qt][2], sacc[2 * u + 1][qt][3])};
-                // V^T operands in batches of VB d-tiles of transposing reads
-                constexpr int VB = S::NDT >= 4 ? 4 : S::NDT;
+                    pb[u][qt] = u32x4_t{pack_bf16x2(sacc[2 * u][qt][0], sacc[2 * u][qt][1]),
+                                        pack_bf16x2(sacc[2 * u][qt][2], sacc[2 * u][qt][3]),
+                                        pack_bf16x2(sacc[2 * u + 1][qt][0], sacc[2 * u + 1][qt][1]),
+                                        pack_bf16x2(sacc[2 * u + 1][qt][2], sacc[2 * u + 1][qt][3])};
+            // V^T operands in batches of VB d-tiles (batch b: 32-key step
+            // u = b / NVB, d-tiles VB (b % NVB) ...); batch b+1 is read
+            // before the MFMAs of batch b.
+            constexpr int VB = S::NDT >= 4 ? 4 : S::NDT;
+            constexpr int NVB = S::NDT / VB;
+            bf16x8_t vfr[2][VB];
+            auto vread = [&](int b, bf16x8_t (&dst)[VB]) __attribute__((always_inline)) {
+                const int u = b / NVB, d0 = (b % NVB) * VB;
 #pragma unroll
-                for (int d0 = 0; d0 < S::NDT; d0 += VB) {
-                    bf16x8_t vfr[VB];
-#pragma unroll
-                    for (int db = 0; db < VB; ++db) {
-                        const int dt = d0 + db;
-                        // keys 32u + 4g + (l16 >> 2) and 16 further
-                        const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4_t*)(Vt + v_lane + (32 * u / S::NB) * D + 16 * dt));
-                        const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_s16x4_t*)(Vt + v_lane + ((32 * u + 16) / S::NB) * D + 16 * dt));
-                        vfr[db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int db = 0; db < VB; ++db) {
-                        o[d0 + db][0] = mfma16(vfr[db], as_bf16x8(pb[0]), o[d0 + db][0]);
-                        o[d0 + db][1] = mfma16(vfr[db], as_bf16x8(pb[1]), o[d0 + db][1]);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
+                for (int db = 0; db < VB; ++db) {
+                    // keys 32u + 4g + (l16 >> 2) and 16 further
+                    const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4_t*)(Vt + v_lane + (32 * u / S::NB) * D + 16 * (d0 + db)));
+                    const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_s16x4_t*)(Vt + v_lane + ((32 * u + 16) / S::NB) * D + 16 * (d0 + db)));
+                    dst[db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
-                o[S::NDT][0] = mfma16(as_bf16x8(wrow[u]), as_bf16x8(pb[0]), o[S::NDT][0]);
-                o[S::NDT][1] = mfma16(as_bf16x8(wrow[u]), as_bf16x8(pb[1]), o[S::NDT][1]);
+            };
+            vread(0, vfr[0]);
+#pragma unroll
+            for (int b = 0; b < 2 * NVB; ++b) {
+                const int u = b / NVB, d0 = (b % NVB) * VB;
+                if (b + 1 < 2 * NVB) vread(b + 1, vfr[(b + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int db = 0; db < VB; ++db) {
+                    o[d0 + db][0] = mfma16(vfr[b & 1][db], as_bf16x8(pb[u][0]), o[d0 + db][0]);
+                    o[d0 + db][1] = mfma16(vfr[b & 1][db], as_bf16x8(pb[u][1]), o[d0 + db][1]);
+                }
+                if (b % NVB == NVB - 1) {
+                    o[S::NDT][0] = mfma16(as_bf16x8(wrow[u]), as_bf16x8(pb[u][0]), o[S::NDT][0]);
+                    o[S::NDT][1] = mfma16(as_bf16x8(wrow[u]), as_bf16x8(pb[u][1]), o[S::NDT][1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
 
         const int TS = T * S::SUB;
-        if (TS > 0) issue(0, K0, V0);
+        if (TS > 0) {
+            w_t = word_of(0, word_raw(0));
+            tile_issue<D, BLK>(source_of(w_t, 0), K0, V0, wave_s, dma_base);
+        }
+        if (TS > 1) w_t1 = word_of(1, word_raw(1));
         for (int t = 0; t < TS; t += 2) {
             step(t, K0, V0, K1, V1, TS);
             if (t + 1 < TS) step(t + 1, K1, V1, K0, V0, TS);
