@@ -155,15 +155,32 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
     }
     __syncthreads();
 
+    // Proxy rows, RG rows per pass over the pooled keys: the compiler keeps
+    // each pass's query quarters in registers, and RG = 4 leaves room for
+    // two waves per SIMD and for the next chunk's keys loading while the
+    // current chunk is scored.
     const int jj = tid >> 2, qq = tid & 3;
-    for (int j0 = 0; j0 < N; j0 += 64) {
-        const int j = j0 + jj;
-        float kv[D / 4];
-        load_kbar_quarter<D>(kbar + ((size_t)h * N + min(j, N - 1)) * D, qq, kv);
+    constexpr int RG = R < 4 ? R : 4;
+    const float* kh = kbar + (size_t)h * N * D;
+#pragma unroll 1
+    for (int g0 = 0; g0 < R; g0 += RG) {
+        float kva[D / 4], kvb[D / 4];
+        auto score = [&](int j0, const float (&kv)[D / 4]) __attribute__((always_inline)) {
+            const int j = j0 + jj;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const float s = proxy_from_quarter<D>(qb[r], kv, qq, c);
-            if (qq == 0 && j < N) rows[r * N + j] = s;
+            for (int r = 0; r < RG; ++r) {
+                const float s = proxy_from_quarter<D>(qb[g0 + r], kv, qq, c);
+                if (qq == 0 && j < N) rows[(g0 + r) * N + j] = s;
+            }
+        };
+        load_kbar_quarter<D>(kh + (size_t)min(jj, N - 1) * D, qq, kva);
+#pragma unroll 1
+        for (int j0 = 0; j0 < N; j0 += 128) {
+            if (j0 + 64 < N) load_kbar_quarter<D>(kh + (size_t)min(j0 + 64 + jj, N - 1) * D, qq, kvb);
+            score(j0, kva);
+            if (j0 + 64 >= N) break;
+            if (j0 + 128 < N) load_kbar_quarter<D>(kh + (size_t)min(j0 + 128 + jj, N - 1) * D, qq, kva);
+            score(j0 + 64, kvb);
         }
     }
     __syncthreads();
