@@ -40,8 +40,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="C3")
     ap.add_argument("--betas", default=None,
-                    help="comma-separated betas; the first is the headline (default: 1.0 then "
-                         "the workload's sweep)")
+                    help="comma-separated betas; the first is the headline (default: the workload's "
+                         "headline beta, then the rest of its sweep)")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -163,7 +163,7 @@ def main():
     binding.lib()
     w = gen.WORKLOADS[args.workload]
     betas = ([float(b) for b in args.betas.split(",")] if args.betas else
-             [1.0] + [b for b in w.betas if b != 1.0])
+             [w.headline_beta] + [b for b in w.betas if b != w.headline_beta])
     H, L, d, B, N = w.H, w.L, w.d, w.B, w.N
     log(f"[bench] generating {w.name}: {w.desc}")
     t = time.perf_counter()
@@ -175,7 +175,10 @@ def main():
     else:
         dev = [torch.from_numpy(a).cuda() for a in (inp.q, inp.k, inp.v)]
     q, k, v = dev
-    del inp
+    if args.no_cpu_baseline:
+        del inp
+    else:  # the oracle sample reads the float32 arrays only
+        inp.q_bits = inp.k_bits = inp.v_bits = None
     out = torch.empty_like(q)
     kept = torch.empty((H, N), dtype=torch.int32, device="cuda")
     ws = binding.alloc_workspace(H, L, d, B, "cuda")

@@ -46,6 +46,7 @@ class Workload:
     seed: int
     grids: Tuple[Tuple[int, int, int], ...]   # latent grids concatenated in order
     text_tokens: int = 0            # N(0,1) tokens appended after the grids
+    headline_beta: float = 1.0      # the beta a benchmark of this workload leads with
     edit_pair: bool = False         # second grid = first grid + 0.2 N(0,1)
     truncate: Optional[int] = None  # keep only the first `truncate` tokens
     desc: str = ""
@@ -88,6 +89,13 @@ WORKLOADS = {
     "C5b": Workload("C5b", H=24, d=64, B=128, dtype="bf16", betas=(NEG_INF, 0.0, 1.0, 3.0), seed=4,
                     grids=((21, 30, 52), (21, 30, 52)), edit_pair=True, truncate=65500,
                     desc="editing-shaped layer at L=65500 (ragged), 24 heads, d=64, B=128, bf16"),
+    # The pages' kernel-level point: 128K tokens at about 90 % sparsity ("Sol-Attn"
+    # visual explainer, "What the paper measured", Figure 5a).  The head count is
+    # not given there; 24 heads keep the host-side arrays near 7 GB.
+    "C6": Workload("C6", H=24, d=128, B=64, dtype="bf16", betas=(1.0, 1.25, 1.5), seed=5,
+                   grids=((32, 64, 64),), headline_beta=1.25,
+                   desc="long-sequence kernel point: 24 heads, 32x64x64 grid, L=131072, d=128, "
+                        "B=64, bf16"),
 }
 
 
