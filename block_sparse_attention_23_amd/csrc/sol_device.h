@@ -105,6 +105,15 @@ struct QbarLds {
     __device__ static int index(int x) { return (x / (D / 4)) * QSTRIDE + (x % (D / 4)); }
 };
 
+// The value of lane (l ^ 1), or (l ^ 2), within each group of four lanes:
+// DPP quad permutations (no LDS round trip).
+__device__ __forceinline__ float quad_xor1(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+}
+
 template <int D>
 __device__ __forceinline__ float proxy_from_quarter(const float* qbar_lds, const float (&kv)[D / 4],
                                                     int qq, float scale) {
@@ -112,8 +121,10 @@ __device__ __forceinline__ float proxy_from_quarter(const float* qbar_lds, const
     float acc = 0.0f;
 #pragma unroll
     for (int e = 0; e < D / 4; ++e) acc = __builtin_fmaf(qp[e], kv[e], acc);
-    const float s01 = acc + __shfl_xor(acc, 1);
-    const float s = s01 + __shfl_xor(s01, 2);
+    // the four lanes of a key add their quarters in the same order:
+    // (q0 + q1) + (q2 + q3), so every lane holds the same sum
+    const float s01 = acc + quad_xor1(acc);
+    const float s = s01 + quad_xor2(s01);
     return s * scale;
 }
 

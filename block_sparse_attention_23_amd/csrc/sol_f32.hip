@@ -89,8 +89,8 @@ __global__ void __launch_bounds__(4 * BLK) attn_f32_kernel(AttnArgs a) {
                 float p = 0.0f;
 #pragma unroll
                 for (int e = 0; e < Q4; ++e) p = __builtin_fmaf(qr[e], kr[e], p);
-                const float p01 = p + __shfl_xor(p, 1);
-                const float s = p01 + __shfl_xor(p01, 2);
+                const float p01 = p + quad_xor1(p);
+                const float s = p01 + quad_xor2(p01);
                 x[t] = wt_s[t] > 0.0f ? s * a.c_log2e : -INFINITY;
                 mx = fmaxf(mx, x[t]);
             }
