@@ -37,11 +37,17 @@ def _load(path):
                                      _dp, _dp]
     L.sol_oracle_merge.argtypes = [_fp, _fp, _fp, _dp, _dp, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int, ctypes.c_int, _u8p, ctypes.c_int64, _i32p, _dp]
+    L.sol_oracle_merge_ex.argtypes = [_fp, _fp, _fp, _dp, _dp, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int, _u8p, ctypes.c_int,
+                                      ctypes.c_int64, _i32p, _dp]
+    L.sol_oracle_route_topk.argtypes = [_dp, _dp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, _dp, _dp, _u8p, _i32p]
     L.sol_oracle_dense.argtypes = [_fp, _fp, _fp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_int64, _i32p, _dp]
     L.sol_oracle_num_threads.argtypes = []
     for f in ("sol_oracle_pool", "sol_oracle_route", "sol_oracle_moments",
-              "sol_oracle_merge", "sol_oracle_dense", "sol_oracle_num_threads"):
+              "sol_oracle_merge", "sol_oracle_merge_ex", "sol_oracle_route_topk",
+              "sol_oracle_dense", "sol_oracle_num_threads"):
         getattr(L, f).restype = ctypes.c_int
     return L
 
@@ -140,8 +146,32 @@ def _rows_arg(rows):
     return rows, rows.shape[0]
 
 
-def merge(q, k, v, kbar, vsum, B, sel, rows=None):
-    """Eq. (9)/(10) merge for every row ([H][L][d]) or for (h, r) pairs ([n][d])."""
+def route_topk(qbar, kbar, k, want_shat=False):
+    """Fixed-budget comparator: the k largest proxy scores of every query
+    block (ties to the lower block index).  Returns a dict with ``sel``,
+    ``kept`` (= k), ``kth`` (the k-th largest score) and optionally ``shat``."""
+    qbar = np.ascontiguousarray(qbar, dtype=np.float64)
+    kbar = np.ascontiguousarray(kbar, dtype=np.float64)
+    H, N, d = qbar.shape
+    out = {"kth": np.empty((H, N)), "sel": np.empty((H, N, N), dtype=np.uint8),
+           "kept": np.empty((H, N), dtype=np.int32),
+           "shat": np.empty((H, N, N)) if want_shat else None}
+    _check(lib().sol_oracle_route_topk(_ptr(qbar, _dp), _ptr(kbar, _dp), H, N, d, int(k),
+                                       _ptr(out["shat"], _dp), _ptr(out["kth"], _dp),
+                                       _ptr(out["sel"], _u8p), _ptr(out["kept"], _i32p)),
+           "route_topk")
+    return out
+
+
+def topk_count(keep_frac, N):
+    """Blocks a fixed-budget row keeps for a kept fraction: round(keep_frac * N)
+    (halves up), clamped to [0, N]."""
+    return int(min(N, max(0, math.floor(keep_frac * N + 0.5))))
+
+
+def merge(q, k, v, kbar, vsum, B, sel, rows=None, drop_approx=False):
+    """Eq. (9)/(10) merge for every row ([H][L][d]) or for (h, r) pairs ([n][d]).
+    drop_approx: leave the unselected blocks out (keep-or-drop)."""
     q, k, v = _f32(q), _f32(k), _f32(v)
     H, L, d = q.shape
     N = nblocks(L, B)
@@ -152,9 +182,10 @@ def merge(q, k, v, kbar, vsum, B, sel, rows=None):
     vsum = np.ascontiguousarray(vsum, dtype=np.float64)
     rows, n = _rows_arg(rows)
     out = np.empty((H, L, d)) if rows is None else np.empty((n, d))
-    _check(lib().sol_oracle_merge(_ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp), _ptr(kbar, _dp),
-                                  _ptr(vsum, _dp), H, L, d, B, _ptr(sel, _u8p), n,
-                                  _ptr(rows, _i32p), _ptr(out, _dp)), "merge")
+    _check(lib().sol_oracle_merge_ex(_ptr(q, _fp), _ptr(k, _fp), _ptr(v, _fp),
+                                     _ptr(kbar, _dp), _ptr(vsum, _dp), H, L, d, B,
+                                     _ptr(sel, _u8p), int(bool(drop_approx)), n,
+                                     _ptr(rows, _i32p), _ptr(out, _dp)), "merge")
     return out
 
 

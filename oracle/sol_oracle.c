@@ -226,6 +226,71 @@ int sol_oracle_moments(const double* qbar, const double* kbar,
 }
 
 /*
+ * Fixed-budget comparator ([ABS]: selecting a fixed fraction of top-ranked
+ * blocks by proxy score imposes fixed budgets): every query block keeps the
+ * k key blocks with the largest proxy scores s_ij = c * qbar_i . kbar_j (the
+ * same proxy as sol_oracle_route), k the same for every (h, i).  Ties in the
+ * score go to the lower block index (the pages do not say).
+ *
+ * Outputs: shat [H][N][N] (may be NULL), kth [H][N] = the k-th largest score
+ * (+inf when k = 0; may be NULL), sel [H][N][N] bytes 0/1 (may be NULL),
+ * kept [H][N] = k (may be NULL).  0 <= k <= N.
+ */
+typedef struct { double s; int j; } score_ix;
+
+static int by_score_then_index(const void* a, const void* b)
+{
+    const score_ix* x = (const score_ix*)a;
+    const score_ix* y = (const score_ix*)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->j > y->j) - (x->j < y->j);
+}
+
+int sol_oracle_route_topk(const double* qbar, const double* kbar, int H, int N, int d, int k,
+                          double* shat, double* kth, uint8_t* sel, int32_t* kept)
+{
+    if (H < 1 || N < 1 || d < 1 || !qbar || !kbar || k < 0 || k > N)
+        return ORACLE_EINVAL;
+    const double c = 1.0 / sqrt((double)d);
+    int err = 0;
+#pragma omp parallel
+    {
+        score_ix* row = (score_ix*)malloc(sizeof(score_ix) * (size_t)N);
+        if (!row) {
+#pragma omp atomic write
+            err = 1;
+        }
+#pragma omp for collapse(2) schedule(static)
+        for (int h = 0; h < H; ++h) {
+            for (int i = 0; i < N; ++i) {
+                if (!row) continue;
+                const double* qi = qbar + ((int64_t)h * N + i) * d;
+                const int64_t base = ((int64_t)h * N + i) * (int64_t)N;
+                for (int j = 0; j < N; ++j) {
+                    const double* kj = kbar + ((int64_t)h * N + j) * d;
+                    double s = 0.0;
+                    for (int x = 0; x < d; ++x) s += qi[x] * kj[x];
+                    row[j].s = c * s;
+                    row[j].j = j;
+                    if (shat) shat[base + j] = c * s;
+                }
+                qsort(row, (size_t)N, sizeof(score_ix), by_score_then_index);
+                if (sel) {
+                    for (int j = 0; j < N; ++j) sel[base + j] = 0;
+                    for (int x = 0; x < k; ++x) sel[base + row[x].j] = 1;
+                }
+                const int64_t hi_idx = (int64_t)h * N + i;
+                if (kth) kth[hi_idx] = k > 0 ? row[k - 1].s : INFINITY;
+                if (kept) kept[hi_idx] = k;
+            }
+        }
+        free(row);
+    }
+    return err ? ORACLE_ENOMEM : ORACLE_OK;
+}
+
+/*
  * Step 3 -- the merge: exact attention over selected blocks and the
  * approximate correction over unselected blocks, in one softmax.
  *
@@ -245,11 +310,17 @@ int sol_oracle_moments(const double* qbar, const double* kbar,
  * sel is [H][N][N] bytes (1 = exact).  rows lists (h, r) pairs (n_rows of
  * them); rows == NULL means every (h, r) in order, and out is then
  * [H][L][d]; otherwise out is [n_rows][d].
+ *
+ * drop_approx != 0 gives the keep-or-drop scheme the pages contrast with
+ * ([VE] "Place it among nearby methods", ordinary block sparse attention:
+ * every unselected block contributes zero; [ABS] "lossy keep-or-drop"): the
+ * terms over U_i are left out of both sums, and a row whose S_i is empty
+ * (D_r = 0) is set to zero (the pages do not say).
  */
-int sol_oracle_merge(const float* q, const float* k, const float* v,
-                     const double* kbar, const double* vsum,
-                     int H, int L, int d, int B, const uint8_t* sel,
-                     int64_t n_rows, const int32_t* rows, double* out)
+int sol_oracle_merge_ex(const float* q, const float* k, const float* v,
+                        const double* kbar, const double* vsum,
+                        int H, int L, int d, int B, const uint8_t* sel, int drop_approx,
+                        int64_t n_rows, const int32_t* rows, double* out)
 {
     if (bad_shape(H, L, d, B) || !q || !k || !v || !kbar || !vsum || !sel || !out)
         return ORACLE_EINVAL;
@@ -292,7 +363,7 @@ int sol_oracle_merge(const float* q, const float* k, const float* v,
                         a_tok[tok] = c * s;
                         if (a_tok[tok] > M) M = a_tok[tok];
                     }
-                } else {
+                } else if (!drop_approx) {
                     const double* kb = kbar + ((int64_t)h * N + j) * d;
                     double s = 0.0;
                     for (int e = 0; e < d; ++e) s += (double)qr[e] * kb[e];
@@ -313,7 +384,7 @@ int sol_oracle_merge(const float* q, const float* k, const float* v,
                         D += w;
                         for (int e = 0; e < d; ++e) num[e] += w * (double)vt[e];
                     }
-                } else {
+                } else if (!drop_approx) {
                     /* approximate term of Eq. (9) / Eq. (10) */
                     const double w = exp(g_blk[j] - M);
                     const double* vs = vsum + ((int64_t)h * N + j) * d;
@@ -322,13 +393,21 @@ int sol_oracle_merge(const float* q, const float* k, const float* v,
                 }
             }
             double* o = out + x * d;
-            for (int e = 0; e < d; ++e) o[e] = num[e] / D;
+            for (int e = 0; e < d; ++e) o[e] = D > 0.0 ? num[e] / D : 0.0;
         }
         free(a_tok);
         free(g_blk);
         free(num);
     }
     return err ? ORACLE_ENOMEM : ORACLE_OK;
+}
+
+int sol_oracle_merge(const float* q, const float* k, const float* v,
+                     const double* kbar, const double* vsum,
+                     int H, int L, int d, int B, const uint8_t* sel,
+                     int64_t n_rows, const int32_t* rows, double* out)
+{
+    return sol_oracle_merge_ex(q, k, v, kbar, vsum, H, L, d, B, sel, 0, n_rows, rows, out);
 }
 
 /*

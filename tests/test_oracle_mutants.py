@@ -35,6 +35,12 @@ PINS = {
     "brute2": lambda: P.test_merge_equals_brute_force_token_logits(200, 32, 16, -0.2),
     "pooled-attn": P.test_beta_plus_inf_is_attention_over_pooled_keys,
     "perm": P.test_permuting_keys_inside_unselected_block_changes_nothing,
+    "topk-count": lambda: P.test_topk_keeps_k_blocks_and_none_scored_below_a_dropped_one(5),
+    "topk-ties": P.test_topk_ties_go_to_the_lower_block_index,
+    "topk-vs-threshold": P.test_topk_at_a_rows_own_count_is_the_threshold_selection,
+    "drop-dense": P.test_drop_with_every_block_selected_is_dense_attention,
+    "drop-brute": lambda: P.test_drop_is_softmax_over_the_selected_tokens_only(100, 16),
+    "drop-empty": P.test_drop_with_nothing_selected_is_zero,
 }
 
 # name -> (text in sol_oracle.c, replacement, replace every occurrence)
@@ -44,7 +50,7 @@ MUTANTS = {
     "key-mean-over-B": ("kb[c] = sk / (double)n;", "kb[c] = sk / (double)B;", False),
     "proxy-unscaled": ("row[j] = c * s;", "row[j] = s;", False),
     "proxy-drops-a-dim": ("for (int x = 0; x < d; ++x) s += qi[x] * kj[x];",
-                          "for (int x = 0; x < d - 1; ++x) s += qi[x] * kj[x];", False),
+                          "for (int x = 0; x < d - 1; ++x) s += qi[x] * kj[x];", True),
     "sample-variance": ("var /= (double)N;", "var /= (double)(N > 1 ? N - 1 : 1);", False),
     "non-strict-threshold": ("const int s_in = row[j] > t;", "const int s_in = row[j] >= t;",
                              False),
@@ -65,6 +71,14 @@ MUTANTS = {
     "query-block-off-by-one": ("const int64_t i = r / B;", "const int64_t i = (r + 1) / B;",
                                False),
     "dense-unscaled": ("s[t] = c * acc;", "s[t] = acc;", False),
+    "topk-ties-to-higher-index": ("return (x->j > y->j) - (x->j < y->j);",
+                                  "return (x->j < y->j) - (x->j > y->j);", False),
+    "topk-keeps-one-fewer": ("for (int x = 0; x < k; ++x) sel[base + row[x].j] = 1;",
+                             "for (int x = 0; x + 1 < k; ++x) sel[base + row[x].j] = 1;", False),
+    "topk-keeps-smallest": ("if (x->s > y->s) return -1;", "if (x->s < y->s) return -1;", False),
+    "drop-keeps-approx-terms": ("} else if (!drop_approx) {\n                    /* approximate",
+                                "} else {\n                    /* approximate", False),
+    "drop-empty-row-nan": ("o[e] = D > 0.0 ? num[e] / D : 0.0;", "o[e] = num[e] / D;", False),
 }
 
 

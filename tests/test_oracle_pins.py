@@ -321,3 +321,94 @@ def test_locality_inputs_route_sanely():
     assert diag > 0.8
     kept = r["kept"].sum() / r["sel"].size
     assert 0.02 < kept < 0.5
+
+
+# ------------------------------------------------- ablations: fixed budget, keep-or-drop
+# The abstract contrasts Sol-Attn with fixed top-ranked budgets and with
+# keep-or-drop sparsification; the explainer's "Place it among nearby methods"
+# says ordinary block sparse attention lets every unselected block contribute
+# zero.  The oracle implements both as comparators.
+
+
+@pytest.mark.parametrize("k", [0, 1, 5, 17, 40])
+def test_topk_keeps_k_blocks_and_none_scored_below_a_dropped_one(k):
+    qbar = rand((2, 40, 12), 30).astype(np.float64)
+    kbar = rand((2, 40, 12), 31).astype(np.float64)
+    r = oracle.route_topk(qbar, kbar, k, want_shat=True)
+    sel = r["sel"].astype(bool)
+    assert (sel.sum(-1) == k).all() and (r["kept"] == k).all()
+    s = r["shat"]
+    if 0 < k < 40:
+        lo_kept = np.where(sel, s, np.inf).min(-1)
+        hi_dropped = np.where(sel, -np.inf, s).max(-1)
+        assert (lo_kept >= hi_dropped).all()
+        np.testing.assert_array_equal(r["kth"], lo_kept)
+    # the scores themselves are the threshold route's proxies
+    np.testing.assert_array_equal(s, oracle.route(qbar, kbar, 1.0, want_shat=True)["shat"])
+
+
+def test_topk_ties_go_to_the_lower_block_index():
+    qbar = rand((1, 12, 6), 32).astype(np.float64)
+    kbar = np.tile(rand((1, 1, 6), 33).astype(np.float64), (1, 12, 1))  # equal scores
+    for k in (0, 1, 5, 12):
+        sel = oracle.route_topk(qbar, kbar, k)["sel"][0]
+        expect = np.zeros(12, np.uint8)
+        expect[:k] = 1
+        assert (sel == expect[None, :]).all()
+
+
+def test_topk_at_a_rows_own_count_is_the_threshold_selection():
+    """Eq. (4) keeps {j : s_ij > tau_i}; with distinct scores that is the
+    kept_i largest, so a fixed budget equal to a row's own count selects the
+    same blocks."""
+    qbar = rand((2, 48, 16), 34).astype(np.float64)
+    kbar = rand((2, 48, 16), 35).astype(np.float64)
+    t = oracle.route(qbar, kbar, 0.7)
+    checked = 0
+    for k in np.unique(t["kept"]):
+        rows = t["kept"] == k
+        tk = oracle.route_topk(qbar, kbar, int(k))
+        assert (tk["sel"][rows] == t["sel"][rows]).all()
+        checked += int(rows.sum())
+    assert checked == 2 * 48
+
+
+def test_topk_count_rounds_half_up():
+    assert [oracle.topk_count(f, 10) for f in (0.0, 0.04, 0.05, 0.149, 0.15, 1.0, 2.0)] == \
+        [0, 0, 1, 1, 2, 10, 10]
+
+
+def test_drop_with_every_block_selected_is_dense_attention():
+    q, k, v = rand((2, 90, 8), 36), rand((2, 90, 8), 37), rand((2, 90, 8), 38)
+    qbar, kbar, vsum = oracle.pool(q, k, v, 16)
+    sel = np.ones((2, 6, 6), np.uint8)
+    out = oracle.merge(q, k, v, kbar, vsum, 16, sel, drop_approx=True)
+    np.testing.assert_allclose(out, textbook_dense(q, k, v), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("L,B", [(100, 16), (64, 8)])
+def test_drop_is_softmax_over_the_selected_tokens_only(L, B):
+    """Brute force: mask the logits of every token outside S_i, softmax, V."""
+    H, d = 2, 8
+    q, k, v = rand((H, L, d), 39), rand((H, L, d), 40), rand((H, L, d), 41)
+    N = (L + B - 1) // B
+    sel = (np.random.default_rng(42).random((H, N, N)) < 0.4).astype(np.uint8)
+    sel[:, :, 0] = 1  # every row keeps at least block 0
+    qbar, kbar, vsum = oracle.pool(q, k, v, B)
+    out = oracle.merge(q, k, v, kbar, vsum, B, sel, drop_approx=True)
+    logits = np.einsum("hrd,htd->hrt", q.astype(np.float64), k.astype(np.float64)) / math.sqrt(d)
+    tok_blk = np.arange(L) // B
+    keep = sel[:, tok_blk][:, :, tok_blk]  # [H][r][t]: block of r selects block of t
+    logits = np.where(keep.astype(bool), logits, -np.inf)
+    ref = np.einsum("hrt,htd->hrd", softmax(logits, axis=-1), v.astype(np.float64))
+    np.testing.assert_allclose(out, ref, rtol=1e-10, atol=1e-12)
+
+
+def test_drop_with_nothing_selected_is_zero():
+    q, k, v = rand((1, 50, 8), 43), rand((1, 50, 8), 44), rand((1, 50, 8), 45)
+    qbar, kbar, vsum = oracle.pool(q, k, v, 16)
+    sel = np.zeros((1, 4, 4), np.uint8)
+    sel[0, 1, 2] = 1  # only query block 1 keeps anything
+    out = oracle.merge(q, k, v, kbar, vsum, 16, sel, drop_approx=True)
+    assert (out[0, :16] == 0).all() and (out[0, 32:] == 0).all()
+    assert np.abs(out[0, 16:32]).max() > 0
