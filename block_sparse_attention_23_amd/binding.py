@@ -13,6 +13,7 @@ import torch
 from . import build as _build
 
 SOL_BF16, SOL_F32 = 0, 1
+SOL_DROP_APPROX, SOL_TOPK = 1, 2
 
 _FUNCS = {
     "sol_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
@@ -29,6 +30,10 @@ _FUNCS = {
                          + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                             ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                             ctypes.c_void_p, ctypes.c_void_p]),
+    "sol_attn_fwd_variant": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4
+                             + [ctypes.c_float, ctypes.c_float, ctypes.c_uint, ctypes.c_int,
+                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "sol_attn_dense": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4
                        + [ctypes.c_void_p, ctypes.c_void_p]),
     "sol_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -191,6 +196,31 @@ def attn_fwd(q, k, v, B, beta, out=None, kept=None, workspace=None, stream=None,
         tau = torch.empty((H, N), dtype=torch.float32, device=q.device)
         _check("sol_attn_fwd_dbg", lib().sol_attn_fwd_dbg(*args, mask.data_ptr(), tau.data_ptr()))
         return out, kept, mask, tau
+
+
+def attn_fwd_variant(q, k, v, B, beta, keep_frac=0.0, drop_approx=False, topk=False, out=None,
+                     kept=None, workspace=None, stream=None):
+    """The forward pass with the pages' comparators (bf16): drop_approx leaves
+    the unselected blocks out (keep-or-drop); topk selects the
+    round(keep_frac * N) largest proxies of every query block instead of the
+    threshold.  Returns (out, kept_counts, sel_mask bits, tau)."""
+    H, L, d = _tokens(q, k, v)
+    N = nblocks(L, B)
+    if out is None:
+        out = torch.empty_like(q)
+    if kept is None:
+        kept = torch.empty((H, N), dtype=torch.int32, device=q.device)
+    if workspace is None:
+        workspace = alloc_workspace(H, L, d, B, q.device)
+    flags = (SOL_DROP_APPROX if drop_approx else 0) | (SOL_TOPK if topk else 0)
+    mask = torch.zeros((H, N, (N + 31) // 32), dtype=torch.int32, device=q.device)
+    tau = torch.empty((H, N), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        _check("sol_attn_fwd_variant", lib().sol_attn_fwd_variant(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), H, L, d, B, float(beta), float(keep_frac),
+            flags, _dtype_code(q), out.data_ptr(), kept.data_ptr(), workspace.data_ptr(),
+            workspace.numel(), _stream_ptr(stream, q.device), mask.data_ptr(), tau.data_ptr()))
+    return out, kept, mask, tau
 
 
 def attn_dense(q, k, v, out=None, stream=None):

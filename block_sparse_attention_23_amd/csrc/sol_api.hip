@@ -102,12 +102,15 @@ sol::AttnArgs sweep_args(const void* q, const void* k, const void* v, const floa
 
 int forward(const void* q, const void* k, const void* v, int H, int L, int d, int B, float beta,
             sol_dtype_t dt, void* out, int32_t* kept, void* ws, size_t ws_bytes, void* stream,
-            uint32_t* sel_mask, float* tau_out) {
+            uint32_t* sel_mask, float* tau_out, float keep_frac = 0.0f, unsigned flags = 0u) {
     int st = check_shape(H, L, d, B);
     if (st != SOL_OK) return st;
     st = check_tensors(q, k, v, out, dt);
     if (st != SOL_OK) return st;
     if (!kept || !aligned(kept, 4) || isnan(beta)) return SOL_EINVAL;
+    if (flags & ~(unsigned)(SOL_DROP_APPROX | SOL_TOPK)) return SOL_EINVAL;
+    if ((flags & SOL_TOPK) && !(keep_frac >= 0.0f && keep_frac <= 1.0f)) return SOL_EINVAL;
+    if (flags && dt != SOL_BF16) return SOL_EUNSUPPORTED;
     if ((sel_mask && !aligned(sel_mask, 4)) || (tau_out && !aligned(tau_out, 4))) return SOL_EINVAL;
     if (!ws || !aligned(ws, kAlign)) return SOL_EWORKSPACE;
     const Workspace w = carve(ws, H, L, d, B);
@@ -125,11 +128,16 @@ int forward(const void* q, const void* k, const void* v, int H, int L, int d, in
     if (sol::launch_pool(q, k, v, bf16, H, L, d, B, w.qbar, w.kbar, w.vsum,
                          bf16 ? w.kbar_bf : nullptr, bf16 ? w.vsum_bf : nullptr, s) != hipSuccess)
         return SOL_EHIP;
-    if (sol::launch_route(w.qbar, w.kbar, H, N, d, c, beta, nullptr, tau, kept, sel, w.queues, s) !=
-        hipSuccess)
+    // fixed budget: round(keep_frac * N), halves up, within [0, N]
+    const int topk = (flags & SOL_TOPK)
+                         ? static_cast<int>(fmin((double)N, fmax(0.0, floor((double)keep_frac * N + 0.5))))
+                         : -1;
+    if (sol::launch_route(w.qbar, w.kbar, H, N, d, c, beta, nullptr, tau, kept, sel, w.queues, s,
+                          topk) != hipSuccess)
         return SOL_EHIP;
-    const sol::AttnArgs a = sweep_args(q, k, v, w.qbar, w.kbar, w.vsum, tau, w.kbar_bf, w.vsum_bf,
-                                       H, L, d, B, out, w.queues, sel);
+    sol::AttnArgs a = sweep_args(q, k, v, w.qbar, w.kbar, w.vsum, tau, w.kbar_bf, w.vsum_bf, H, L,
+                                 d, B, out, w.queues, sel);
+    a.drop_approx = (flags & SOL_DROP_APPROX) ? 1 : 0;
     if (launch_sweep(a, bf16, d, B, false, s) != hipSuccess) return SOL_EHIP;
     return SOL_OK;
 }
@@ -234,6 +242,14 @@ int sol_attn_fwd_dbg(const void* q, const void* k, const void* v, int H, int L, 
                      size_t ws_bytes, void* stream, uint32_t* sel_mask, float* tau) {
     return forward(q, k, v, H, L, d, B, beta, dt, out, kept_counts, workspace, ws_bytes, stream,
                    sel_mask, tau);
+}
+
+int sol_attn_fwd_variant(const void* q, const void* k, const void* v, int H, int L, int d, int B,
+                         float beta, float keep_frac, unsigned flags, sol_dtype_t dt, void* out,
+                         int32_t* kept_counts, void* workspace, size_t ws_bytes, void* stream,
+                         uint32_t* sel_mask, float* tau) {
+    return forward(q, k, v, H, L, d, B, beta, dt, out, kept_counts, workspace, ws_bytes, stream,
+                   sel_mask, tau, keep_frac, flags);
 }
 
 int sol_attn_dense(const void* q, const void* k, const void* v, int H, int L, int d, sol_dtype_t dt,

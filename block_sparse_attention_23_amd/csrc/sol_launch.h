@@ -24,6 +24,7 @@ struct AttnArgs {
     int nlast;           // valid tokens in the last block
     float c;             // 1/sqrt(d): proxy-score scale
     float c_log2e;       // 1/sqrt(d) * log2(e): attention logits in base 2
+    int drop_approx;     // bf16 sweep: leave the unselected blocks out (keep-or-drop)
 };
 
 // Each returns hipSuccess or the launch error.
@@ -34,9 +35,12 @@ hipError_t launch_pooled_to_bf16(const float* kbar, const float* vsum, size_t n,
                                  uint16_t* vsum_bf, int* queues, hipStream_t s);
 // Proxy rows, thresholds (computed, or taken from tau_in when it is not
 // null), kept counts and selection bits (when sel is not null).
+// topk >= 0: the fixed-budget comparator instead of the threshold rule
+// (the k = topk largest scores of every row, ties to the lower index;
+// tau = the k-th largest score); beta and tau_in are then unused.
 hipError_t launch_route(const float* qbar, const float* kbar, int H, int N, int d, float c,
                         float beta, const float* tau_in, float* tau, int32_t* kept, uint32_t* sel,
-                        int* queues, hipStream_t s);
+                        int* queues, hipStream_t s, int topk = -1);
 hipError_t launch_sweep_bf16(const AttnArgs& a, int d, int B, bool dense, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int d, int B, bool dense, hipStream_t s);
 hipError_t launch_reset_counters(int* queues, hipStream_t s);

@@ -133,6 +133,62 @@ __global__ void __launch_bounds__(256) pooled_to_bf16_kernel(const float* __rest
 // R rows; the rows live in dynamic LDS only.  Each s_ij is computed with the
 // shared four-lane routine, exactly as the sweep recomputes it.
 // ============================================================================
+// Fixed-budget selection, the comparator the abstract contrasts Sol-Attn
+// with (a fixed fraction of top-ranked blocks by proxy score): each of the
+// nr rows keeps its k largest scores, ties to the lower block index.  Wave
+// w ranks rows w, w + 4, ... held in LDS: the k-th largest score is found
+// exactly by a binary search over order-preserving 32-bit keys (counts from
+// ballots), then every larger score is kept, and of the scores equal to it
+// the lowest-index ones until k are kept.  tau = that k-th largest score
+// (+inf for k = 0); kept = k.
+__device__ __forceinline__ uint32_t order_key(float s) {
+    const uint32_t b = __float_as_uint(s + 0.0f);  // -0 counts as +0
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float order_key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ void route_rows_topk(const float* rows, int N, int nr, int k, int wave, int lane,
+                                uint32_t* sel, int W, float* tau, int32_t* kept) {
+    for (int r = wave; r < nr; r += 4) {
+        const float* row = rows + r * N;
+        uint32_t T = 0;  // largest key with at least k keys >= it
+        for (int b = 31; b >= 0; --b) {
+            const uint32_t cand = T | (1u << b);
+            int cnt = 0;
+            for (int j0 = 0; j0 < N; j0 += 64) {
+                const int j = j0 + lane;
+                cnt += __popcll(__ballot(j < N && order_key(row[j]) >= cand));
+            }
+            if (cnt >= k) T = cand;
+        }
+        int above = 0;
+        for (int j0 = 0; j0 < N; j0 += 64) {
+            const int j = j0 + lane;
+            above += __popcll(__ballot(j < N && order_key(row[j]) > T));
+        }
+        const int need = k - above;  // keys equal to T still to keep
+        uint32_t* srow = sel ? sel + (size_t)r * W : nullptr;
+        int seen = 0, cnt = 0;
+        for (int j0 = 0; j0 < N; j0 += 64) {
+            const int j = j0 + lane;
+            const uint32_t kj = j < N ? order_key(row[j]) : 0u;
+            const uint64_t eq = __ballot(j < N && kj == T);
+            const int rank = seen + __popcll(eq & ((1ull << lane) - 1ull));
+            const uint64_t m = __ballot(j < N && (kj > T || (kj == T && rank < need)));
+            seen += __popcll(eq);
+            cnt += __popcll(m);
+            const int w0 = j0 >> 5;
+            if (srow && lane < 2 && w0 + lane < W) srow[w0 + lane] = static_cast<uint32_t>(m >> (32 * lane));
+        }
+        if (lane == 0) {
+            tau[r] = k > 0 ? order_key_value(T) : INFINITY;
+            kept[r] = cnt;
+        }
+    }
+}
+
 template <int D, int R>
 __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qbar,
                                                     const float* __restrict__ kbar, int N,
@@ -141,7 +197,7 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
                                                     float* __restrict__ tau_out,
                                                     int32_t* __restrict__ kept,
                                                     uint32_t* __restrict__ sel, int W,
-                                                    int* __restrict__ queues) {
+                                                    int* __restrict__ queues, int topk) {
     extern __shared__ float rows[];  // [R][N]
     __shared__ float qb[R][QbarLds<D>::SIZE];
     const int h = blockIdx.x / groups_per_head;
@@ -185,6 +241,11 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
     }
     __syncthreads();
 
+    if (topk >= 0) {
+        route_rows_topk(rows, N, nr, topk, wave, lane, sel ? sel + ((size_t)h * N + i0) * W : nullptr,
+                        W, tau_out + (size_t)h * N + i0, kept + (size_t)h * N + i0);
+        return;
+    }
     // statistics: wave w handles rows w, w+4, ... (lane-strided sums in a
     // fixed order, then a butterfly whose result every lane shares)
     for (int r = wave; r < nr; r += 4) {
@@ -247,21 +308,21 @@ hipError_t pool_t(const void* q, const void* k, const void* v, int bf16, int H, 
 template <int D, int R>
 hipError_t route_t(const float* qbar, const float* kbar, int H, int N, float c, float beta,
                    const float* tau_in, float* tau, int32_t* kept, uint32_t* sel, int* queues,
-                   hipStream_t s) {
+                   int topk, hipStream_t s) {
     const int gph = (N + R - 1) / R;
     const size_t shm = sizeof(float) * (size_t)R * N;
     hipLaunchKernelGGL((route_kernel<D, R>), dim3(H * gph), dim3(256), shm, s, qbar, kbar, N, gph, c,
-                       beta, tau_in, tau, kept, sel, (N + 31) / 32, queues);
+                       beta, tau_in, tau, kept, sel, (N + 31) / 32, queues, topk);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t route_d(const float* qbar, const float* kbar, int H, int N, float c, float beta,
                    const float* tau_in, float* tau, int32_t* kept, uint32_t* sel, int* queues,
-                   hipStream_t s) {
+                   int topk, hipStream_t s) {
     // as many rows per workgroup as 64 KB of LDS holds
     const size_t row_bytes = sizeof(float) * ((size_t)N + QbarLds<D>::SIZE);
-#define SOL_ROUTE(R) route_t<D, R>(qbar, kbar, H, N, c, beta, tau_in, tau, kept, sel, queues, s)
+#define SOL_ROUTE(R) route_t<D, R>(qbar, kbar, H, N, c, beta, tau_in, tau, kept, sel, queues, topk, s)
     if (16 * row_bytes <= 65536) return SOL_ROUTE(16);
     if (8 * row_bytes <= 65536) return SOL_ROUTE(8);
     if (4 * row_bytes <= 65536) return SOL_ROUTE(4);
@@ -299,9 +360,9 @@ hipError_t launch_reset_counters(int* queues, hipStream_t s) {
 
 hipError_t launch_route(const float* qbar, const float* kbar, int H, int N, int d, float c,
                         float beta, const float* tau_in, float* tau, int32_t* kept, uint32_t* sel,
-                        int* queues, hipStream_t s) {
-    if (d == 64) return route_d<64>(qbar, kbar, H, N, c, beta, tau_in, tau, kept, sel, queues, s);
-    if (d == 128) return route_d<128>(qbar, kbar, H, N, c, beta, tau_in, tau, kept, sel, queues, s);
+                        int* queues, hipStream_t s, int topk) {
+    if (d == 64) return route_d<64>(qbar, kbar, H, N, c, beta, tau_in, tau, kept, sel, queues, topk, s);
+    if (d == 128) return route_d<128>(qbar, kbar, H, N, c, beta, tau_in, tau, kept, sel, queues, topk, s);
     return hipErrorInvalidValue;
 }
 

@@ -254,8 +254,9 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             __syncthreads();
             if (wave == 0) {
                 int nt = 0;
-                // approximate chunks that hold an unselected block of a query block
-                for (int c0 = 0; c0 < NC; c0 += 64) {
+                // approximate chunks that hold an unselected block of a query
+                // block (none when the unselected blocks are dropped)
+                for (int c0 = 0; c0 < (a.drop_approx ? 0 : NC); c0 += 64) {
                     const int c = c0 + lane;
                     uint32_t part = 0;
                     if (c < NC) {
@@ -554,7 +555,7 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             for (int qt = 0; qt < 2; ++qt) {
                 // row 0 of the weight tile sits in element 0 of lanes 0..15
                 const float lt = __shfl(o[S::NDT][qt][0], l16);
-                const float inv = 1.0f / lt;
+                const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;  // 0: nothing kept (keep-or-drop)
                 const int row = q0 + wave * 32 + qt * 16 + l16;
                 if (row < L) {
                     u16* dst = og + head_off + (size_t)row * D + g * 4;

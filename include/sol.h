@@ -152,6 +152,33 @@ int sol_attn_fwd_dbg(const void* q, const void* k, const void* v,
                      uint32_t* sel_mask, float* tau);
 
 /*
+ * The forward pass with the comparators the pages contrast Sol-Attn with,
+ * for accuracy studies (abstract: "selecting a fixed fraction of top-ranked
+ * blocks by proxy score imposes fixed budgets" and "lossy keep-or-drop
+ * sparsification"; visual explainer, "Place it among nearby methods":
+ * ordinary block sparse attention lets every unselected block contribute
+ * zero).  flags is a bitwise OR of:
+ *   SOL_DROP_APPROX  unselected blocks contribute nothing (no Eq. (9) /
+ *                    Eq. (10) approximate terms); a row whose selection is
+ *                    empty is written as zeros.
+ *   SOL_TOPK         every query block selects the k = round(keep_frac * N)
+ *                    blocks (halves up, within [0, N]) with the largest proxy
+ *                    scores, ties to the lower block index, instead of
+ *                    s_ij > tau_i; beta is ignored, tau receives the k-th
+ *                    largest score (+inf for k = 0) and kept_counts = k.
+ * flags = 0 is sol_attn_fwd_dbg.  Other arguments as sol_attn_fwd_dbg.
+ * Errors: unknown flag bits, or SOL_TOPK with keep_frac outside [0, 1] or
+ * NaN: SOL_EINVAL; nonzero flags with SOL_F32: SOL_EUNSUPPORTED.
+ */
+#define SOL_DROP_APPROX 1u
+#define SOL_TOPK 2u
+int sol_attn_fwd_variant(const void* q, const void* k, const void* v,
+                         int H, int L, int d, int B, float beta, float keep_frac,
+                         unsigned flags, sol_dtype_t dt, void* out, int32_t* kept_counts,
+                         void* workspace, size_t ws_bytes, void* stream,
+                         uint32_t* sel_mask, float* tau);
+
+/*
  * Dense softmax attention softmax(Q K^T / sqrt(d)) V (the pages' speedup
  * baseline, "Sol-Attn" visual explainer, "What the paper measured": dense
  * attention wall time over the method's), on the same tile machinery with

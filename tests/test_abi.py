@@ -32,7 +32,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "sol_attn_dense", "sol_attn_fwd", "sol_attn_fwd_dbg", "sol_pool", "sol_route",
+        "sol_attn_dense", "sol_attn_fwd", "sol_attn_fwd_dbg", "sol_attn_fwd_variant", "sol_pool",
+        "sol_route",
         "sol_status_string", "sol_sweep", "sol_workspace_bytes"])
 
 
@@ -134,3 +135,18 @@ def test_unpack_mask_bit_order():
     assert list(np.nonzero(bits[0, 0])[0]) == [0, 1, 3]
     m2 = torch.tensor([[[0, 1]]], dtype=torch.int32)
     assert list(np.nonzero(binding.unpack_mask(m2, 40)[0, 0])[0]) == [32]
+
+
+def test_variant_rejects_bad_flags_and_fractions(lib):
+    # (q, k, v, H, L, d, B, beta, keep_frac, flags, dt, out, kept, ws, ws_bytes, stream, mask, tau)
+    ok = [FAKE, FAKE, FAKE, 1, 100, 64, 64, 1.0, 0.5, 0, 0, FAKE, FAKE, FAKE_WS, 1 << 30, None,
+          None, None]
+    for i, val, want in [(9, 4, -1), (9, 2 | 8, -1), (8, math.nan, -1), (8, -0.1, -1),
+                         (8, 1.5, -1), (10, 1, -2)]:
+        bad = list(ok)
+        bad[i] = val
+        if i == 10:
+            bad[9] = 1  # drop with fp32 inputs
+        if i == 8:
+            bad[9] = 2  # the fraction matters for the fixed budget only
+        assert lib.sol_attn_fwd_variant(*bad) == want, (i, val)
