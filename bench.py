@@ -43,6 +43,10 @@ def parse():
                     help="comma-separated betas; the first is the headline (default: the workload's "
                          "headline beta, then the rest of its sweep)")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--ablation", action="store_true",
+                    help="instead of the benchmark line: error against dense attention and time "
+                         "per forward of Sol-Attn, keep-or-drop and a fixed top-k budget at "
+                         "equal kept fraction, per beta (one JSON line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
@@ -145,6 +149,57 @@ def cpu_baseline(w, inp, beta, target_s):
     }
 
 
+def ablation(args, np, torch, binding, gen):
+    """What the approximate correction buys: for each beta, relative L2 error
+    against the in-library dense attention and time per forward of
+      sol        Sol-Attn (threshold selection, approximate correction),
+      drop       the same selection, unselected blocks left out (keep-or-drop),
+      topk       a fixed budget of round(rho N) blocks per query block, rho =
+                 Sol-Attn's kept fraction at that beta, with the correction,
+      topk_drop  the fixed budget without it.
+    The dense reference is itself bf16 (a ~0.3 % rounding floor)."""
+    w = gen.WORKLOADS[args.workload]
+    betas = ([float(b) for b in args.betas.split(",")] if args.betas else list(w.betas))
+    log(f"[ablation] generating {w.name}: {w.desc}")
+    inp = gen.generate(w)
+    q, k, v = [torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+               for b in (inp.q_bits, inp.k_bits, inp.v_bits)]
+    del inp
+    ws = binding.alloc_workspace(w.H, w.L, w.d, w.B, "cuda")
+    ref = binding.attn_dense(q, k, v).float()
+    ref_norm = torch.linalg.vector_norm(ref).item()
+    out = torch.empty_like(q)
+
+    def err(o):
+        return torch.linalg.vector_norm(o.float() - ref).item() / ref_norm
+
+    rows = []
+    for beta in betas:
+        _, kept = binding.attn_fwd(q, k, v, w.B, beta, out=out, workspace=ws)
+        rho = kept.sum().item() / (w.H * w.N * w.N)
+        runs = {
+            "sol": lambda: binding.attn_fwd(q, k, v, w.B, beta, out=out, workspace=ws),
+            "drop": lambda: binding.attn_fwd_variant(q, k, v, w.B, beta, drop_approx=True,
+                                                     out=out, workspace=ws),
+            "topk": lambda: binding.attn_fwd_variant(q, k, v, w.B, beta, keep_frac=rho, topk=True,
+                                                     out=out, workspace=ws),
+            "topk_drop": lambda: binding.attn_fwd_variant(q, k, v, w.B, beta, keep_frac=rho,
+                                                          topk=True, drop_approx=True, out=out,
+                                                          workspace=ws),
+        }
+        row = {"beta": beta, "kept_frac": rho}
+        for name, fn in runs.items():
+            ms, _ = time_loop(fn, args.steps, args.warmup, torch)
+            fn()
+            torch.cuda.synchronize()
+            row[name] = {"rel_l2_err": err(out), "ms": ms}
+        log(f"[ablation] beta={beta} kept={rho:.4f} " +
+            ", ".join(f"{n}: err {row[n]['rel_l2_err']:.4f} {row[n]['ms']:.2f} ms" for n in runs))
+        rows.append(row)
+    print(json.dumps({"ablation": w.name, "reference": "in-library dense attention (bf16)",
+                      "error": "relative L2 over all outputs", "rows": rows}))
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -161,6 +216,8 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     binding.lib()
+    if args.ablation:
+        return ablation(args, np, torch, binding, gen)
     w = gen.WORKLOADS[args.workload]
     betas = ([float(b) for b in args.betas.split(",")] if args.betas else
              [w.headline_beta] + [b for b in w.betas if b != w.headline_beta])
