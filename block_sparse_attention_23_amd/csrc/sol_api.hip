@@ -91,7 +91,6 @@ sol::AttnArgs sweep_args(const void* q, const void* k, const void* v, const floa
     a.kbar_bf = kbar_bf; a.vsum_bf = vsum_bf;
     a.out = out;
     a.sel = sel;
-    a.sel_dbg = nullptr;
     a.queues = counters;
     a.H = H; a.L = L; a.N = N; a.W = (N + 31) / 32;
     a.nlast = L - (N - 1) * B;

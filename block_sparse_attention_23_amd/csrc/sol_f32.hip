@@ -1,6 +1,8 @@
 // sol_f32.hip -- the Sol-Attn sweep for fp32 inputs (vector ALU, fp32
-// arithmetic throughout; the path that meets the fp32 tolerance).  Same
-// routing arithmetic, tile order rule and merge as the bf16 sweep.
+// arithmetic throughout; the path that meets the fp32 tolerance).  It takes
+// its decisions itself, s_ij > tau_i with the routing kernel's thresholds
+// and the same four-lane proxy arithmetic, so they equal the routing
+// kernel's bits; the merge is the bf16 sweep's.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -14,7 +16,7 @@ namespace sol {
 // attention sweep, fp32 inputs (vector ALU; exact fp32 arithmetic path)
 // ============================================================================
 // Four consecutive lanes own one query row; lane quarter qq holds d/4 of its
-// query and output columns.  The same routing arithmetic as the bf16 kernel.
+// query and output columns.  Proxy scores use the routing kernel's routine.
 template <int D, int BLK, bool DENSE>
 __global__ void __launch_bounds__(4 * BLK) attn_f32_kernel(AttnArgs a) {
     constexpr int NT = 4 * BLK;
@@ -150,12 +152,6 @@ __global__ void __launch_bounds__(4 * BLK) attn_f32_kernel(AttnArgs a) {
                         const int pos = base + __popcll(msk & ((1ull << lane) - 1ull));
                         if (sel) sel_list[pos] = j0 + jj;
                         base += __popcll(msk);
-                        if (a.sel_dbg) {
-                            const int w0 = (j0 + hh * 64) >> 5;
-                            uint32_t* dst = a.sel_dbg + (size_t)item * a.W;
-                            if (lane == 0 && w0 < a.W) dst[w0] = static_cast<uint32_t>(msk);
-                            if (lane == 1 && w0 + 1 < a.W) dst[w0 + 1] = static_cast<uint32_t>(msk >> 32);
-                        }
                     }
                     if (lane == 0) misc_s[1] = base;
                 }

@@ -18,7 +18,6 @@ struct AttnArgs {
     const uint16_t* vsum_bf;  // [H][N][d] bf16 copy of vsum
     void* out;
     const uint32_t* sel; // [H][N][W] selection bits of the routing kernel (bf16 sweep)
-    uint32_t* sel_dbg;   // [H][N][W] or null (fp32 path: written by the sweep)
     int* queues;         // 8 per-XCD work counters (sol only)
     int H, L, N, W;
     int nlast;           // valid tokens in the last block

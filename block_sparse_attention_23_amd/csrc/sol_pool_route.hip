@@ -131,7 +131,9 @@ __global__ void __launch_bounds__(256) pooled_to_bf16_kernel(const float* __rest
 // |{j : s_ij > tau_i}| (Eq. (4)).  One workgroup (256 threads) serves R
 // consecutive query blocks of one head, so each pooled key is read once per
 // R rows; the rows live in dynamic LDS only.  Each s_ij is computed with the
-// shared four-lane routine, exactly as the sweep recomputes it.
+// shared four-lane routine, which the fp32 sweep also uses for its own
+// decisions.  The decisions leave as bits (one ballot per 64 key blocks),
+// read by the bf16 sweep.
 // ============================================================================
 // Fixed-budget selection, the comparator the abstract contrasts Sol-Attn
 // with (a fixed fraction of top-ranked blocks by proxy score): each of the

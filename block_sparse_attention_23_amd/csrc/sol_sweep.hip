@@ -15,8 +15,13 @@
 //      blocks that use it.
 //   2. the tile loop over 64-key tiles.  Tiles stream from HBM straight into
 //      LDS (direct-to-LDS buffer loads, 16 bytes a lane) into two buffers, so
-//      the next tile loads while the current one is computed; K and V rows
-//      sit in padded 1 KB LDS blocks (layout below).  Scores are formed
+//      the next tile loads while the current one is computed; the loads are
+//      issued right after the barrier that opens a step (the tile-list words
+//      are carried one step ahead in scalar registers), by all four waves,
+//      or by the two waves of a query block that skips the current tile.
+//      K and V rows sit in padded 1 KB LDS blocks (layout below), and each
+//      batch of K or V fragment reads is issued before the MFMAs of the
+//      batch before it.  Scores are formed
 //      transposed, S^T = K Q^T (each lane: one query row per 16-row tile, 4
 //      keys per 16-key tile), and O^T += V^T P^T takes V^T through the
 //      transposing LDS read (ds_read_b64_tr_b16) and P^T from registers.
@@ -79,16 +84,6 @@ constexpr uint32_t kIndexMask = (1u << kPartShift) - 1u;
 // transposing V reads are conflict-free at d = 64 and d = 128 (at d = 64 a
 // K read still meets one conflict in four cycles: no uniform padding of the
 // eight 1 KB blocks avoids it).
-
-// Keep bits 0, 4, 8, ..., 60 of m and pack them into bits 0..15.
-__device__ __forceinline__ uint32_t every_fourth_bit(uint64_t m) {
-    uint64_t x = m & 0x1111111111111111ull;
-    x = (x | (x >> 3)) & 0x0303030303030303ull;
-    x = (x | (x >> 6)) & 0x000F000F000F000Full;
-    x = (x | (x >> 12)) & 0x000000FF000000FFull;
-    x = (x | (x >> 24)) & 0xFFFFull;
-    return static_cast<uint32_t>(x);
-}
 
 // Direct-to-LDS loads of a tile: load i of wave w fills block b = w*LPT + i
 // of the K (and of the V) buffer -- lane l writes bytes 16 l .. 16 l + 15 of
