@@ -75,12 +75,8 @@ __device__ __forceinline__ float wave_sum_xor16_32(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// Proxy score s_ij = qbar_i . kbar_j / sqrt(d) ("Sol-Attn" visual explainer,
-// Eq. (11) right-hand side), computed by four consecutive lanes: lane quarter
-// qq sums d/4 products in index order with fused multiply-adds, then the
-// quarters are combined as (p0 + p1) + (p2 + p3).  The routing kernel and the
-// fp32 attention kernel both call exactly these two functions with the same
-// operands, so both see bit-identical scores and take identical decisions.
+// Quarter qq (d/4 consecutive floats) of a pooled row, for four lanes that
+// share a row: the fp32 sweep's approximate operands.
 // ---------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ void load_kbar_quarter(const float* __restrict__ row, int qq,
@@ -96,15 +92,6 @@ __device__ __forceinline__ void load_kbar_quarter(const float* __restrict__ row,
     }
 }
 
-// qbar in LDS is stored in four quarters of D/4 floats at a stride of
-// QSTRIDE = D/4 + 1, so the four lanes of a key read four different banks.
-template <int D>
-struct QbarLds {
-    static constexpr int QSTRIDE = D / 4 + 1;
-    static constexpr int SIZE = 4 * QSTRIDE;
-    __device__ static int index(int x) { return (x / (D / 4)) * QSTRIDE + (x % (D / 4)); }
-};
-
 // The value of lane (l ^ 1), or (l ^ 2), within each group of four lanes:
 // DPP quad permutations (no LDS round trip).
 __device__ __forceinline__ float quad_xor1(float x) {
@@ -112,20 +99,6 @@ __device__ __forceinline__ float quad_xor1(float x) {
 }
 __device__ __forceinline__ float quad_xor2(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-}
-
-template <int D>
-__device__ __forceinline__ float proxy_from_quarter(const float* qbar_lds, const float (&kv)[D / 4],
-                                                    int qq, float scale) {
-    const float* qp = qbar_lds + qq * QbarLds<D>::QSTRIDE;
-    float acc = 0.0f;
-#pragma unroll
-    for (int e = 0; e < D / 4; ++e) acc = __builtin_fmaf(qp[e], kv[e], acc);
-    // the four lanes of a key add their quarters in the same order:
-    // (q0 + q1) + (q2 + q3), so every lane holds the same sum
-    const float s01 = acc + quad_xor1(acc);
-    const float s = s01 + quad_xor2(s01);
-    return s * scale;
 }
 
 // Persistent-kernel work queues: eight counters, one per XCD (workgroup w

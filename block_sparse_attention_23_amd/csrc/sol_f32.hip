@@ -1,8 +1,7 @@
 // sol_f32.hip -- the Sol-Attn sweep for fp32 inputs (vector ALU, fp32
-// arithmetic throughout; the path that meets the fp32 tolerance).  It takes
-// its decisions itself, s_ij > tau_i with the routing kernel's thresholds
-// and the same four-lane proxy arithmetic, so they equal the routing
-// kernel's bits; the merge is the bf16 sweep's.
+// arithmetic throughout; the path that meets the fp32 tolerance).  Like the
+// bf16 sweep it takes its decisions from the routing kernel's bits; the
+// merge is the bf16 sweep's.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -16,7 +15,7 @@ namespace sol {
 // attention sweep, fp32 inputs (vector ALU; exact fp32 arithmetic path)
 // ============================================================================
 // Four consecutive lanes own one query row; lane quarter qq holds d/4 of its
-// query and output columns.  Proxy scores use the routing kernel's routine.
+// query and output columns.
 template <int D, int BLK, bool DENSE>
 __global__ void __launch_bounds__(4 * BLK) attn_f32_kernel(AttnArgs a) {
     constexpr int NT = 4 * BLK;
@@ -24,7 +23,6 @@ __global__ void __launch_bounds__(4 * BLK) attn_f32_kernel(AttnArgs a) {
     constexpr int KP = D + 4;  // pitch keeps 16-byte alignment
     __shared__ __align__(16) float Kf[BLK * KP];
     __shared__ __align__(16) float Vf[BLK * KP];
-    __shared__ __align__(16) float qb_s[QbarLds<D>::SIZE];
     __shared__ float wt_s[BLK];            // column weight; 0 = masked column
     __shared__ int sel_list[BLK];
     __shared__ unsigned char flag_s[BLK];
@@ -71,11 +69,7 @@ __global__ void __launch_bounds__(4 * BLK) attn_f32_kernel(AttnArgs a) {
                 qr[4 * e] = t.x; qr[4 * e + 1] = t.y; qr[4 * e + 2] = t.z; qr[4 * e + 3] = t.w;
             }
         }
-        float tau_i = 0.0f;
-        if (!DENSE) {
-            for (int t = tid; t < D; t += NT) qb_s[QbarLds<D>::index(t)] = a.qbar[(size_t)item * D + t];
-            tau_i = a.tau[item];
-        }
+        const uint32_t* srow = DENSE ? nullptr : a.sel + (size_t)item * a.W;  // bit j: s_ij > tau_i
         float m_run = -INFINITY, l_run = 0.0f;
         float acc[Q4];
 #pragma unroll
@@ -126,8 +120,8 @@ __global__ void __launch_bounds__(4 * BLK) attn_f32_kernel(AttnArgs a) {
                     const bool valid = jj < nj;
                     float kv[D / 4];
                     load_kbar_quarter<D>(a.kbar + ((size_t)h * N + jc) * D, qq, kv);
-                    const float s = proxy_from_quarter<D>(qb_s, kv, qq, a.c);
-                    const bool sel = valid && (s > tau_i);
+                    const int jg = j0 + jj;
+                    const bool sel = valid && ((srow[jg >> 5] >> (jg & 31)) & 1u);
                     if (qq == 0) {
                         flag_s[jj] = sel ? 1 : (valid ? 0 : 2);
                         wt_s[jj] = (valid && !sel)

@@ -129,11 +129,10 @@ __global__ void __launch_bounds__(256) pooled_to_bf16_kernel(const float* __rest
 // blocks (Eq. (11) right-hand side), its population mean and standard
 // deviation (Eq. (5)), tau_i = mu_i + beta sigma_i and the kept count
 // |{j : s_ij > tau_i}| (Eq. (4)).  One workgroup (256 threads) serves R
-// consecutive query blocks of one head, so each pooled key is read once per
-// R rows; the rows live in dynamic LDS only.  Each s_ij is computed with the
-// shared four-lane routine, which the fp32 sweep also uses for its own
-// decisions.  The decisions leave as bits (one ballot per 64 key blocks),
-// read by the bf16 sweep.
+// consecutive query blocks of one head (R <= 16: one MFMA row tile), so each
+// pooled key is read once per R rows; the rows live in dynamic LDS only.
+// The decisions leave as bits (one ballot per 64 key blocks), which both
+// sweeps read: the routing kernel is the one place s_ij is formed.
 // ============================================================================
 // Fixed-budget selection, the comparator the abstract contrasts Sol-Attn
 // with (a fixed fraction of top-ranked blocks by proxy score): each of the
@@ -201,45 +200,58 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
                                                     uint32_t* __restrict__ sel, int W,
                                                     int* __restrict__ queues, int topk) {
     extern __shared__ float rows[];  // [R][N]
-    __shared__ float qb[R][QbarLds<D>::SIZE];
     const int h = blockIdx.x / groups_per_head;
     const int i0 = (blockIdx.x % groups_per_head) * R;
     const int nr = min(R, N - i0);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     if (queues && blockIdx.x == 0 && tid < 8) queues[tid] = 0;
-    for (int t = tid; t < R * D; t += 256) {
-        const int r = t / D, x = t % D;
-        qb[r][QbarLds<D>::index(x)] = r < nr ? qbar[((size_t)h * N + i0 + r) * D + x] : 0.0f;
-    }
-    __syncthreads();
 
-    // Proxy rows, RG rows per pass over the pooled keys: the compiler keeps
-    // each pass's query quarters in registers, and RG = 4 leaves room for
-    // two waves per SIMD and for the next chunk's keys loading while the
-    // current chunk is scored.
-    const int jj = tid >> 2, qq = tid & 3;
-    constexpr int RG = R < 4 ? R : 4;
-    const float* kh = kbar + (size_t)h * N * D;
-#pragma unroll 1
-    for (int g0 = 0; g0 < R; g0 += RG) {
-        float kva[D / 4], kvb[D / 4];
-        auto score = [&](int j0, const float (&kv)[D / 4]) __attribute__((always_inline)) {
-            const int j = j0 + jj;
+    // Proxy rows by fp32 MFMA (v_mfma_f32_16x16x4_f32): the workgroup's
+    // rows are one 16-row tile (rows past R or N are formed and not kept);
+    // wave w takes 16-key tiles w, w + 4, ...  Lane (l16, g) feeds the MFMA
+    // its row's (A) and its key's (B) entries d = g D/4 + s at step s, the
+    // same order of d on both sides, so the 32 steps contract all of d.  The
+    // next key tile's entries load while the current one is multiplied.
+    const int l16 = lane & 15, g = lane >> 4;
+    constexpr int QD = D / 4;
+    float qv[QD];
+    {
+        const float4* src = reinterpret_cast<const float4*>(
+            qbar + ((size_t)h * N + min(i0 + l16, N - 1)) * D + g * QD);
 #pragma unroll
-            for (int r = 0; r < RG; ++r) {
-                const float s = proxy_from_quarter<D>(qb[g0 + r], kv, qq, c);
-                if (qq == 0 && j < N) rows[(g0 + r) * N + j] = s;
-            }
-        };
-        load_kbar_quarter<D>(kh + (size_t)min(jj, N - 1) * D, qq, kva);
-#pragma unroll 1
-        for (int j0 = 0; j0 < N; j0 += 128) {
-            if (j0 + 64 < N) load_kbar_quarter<D>(kh + (size_t)min(j0 + 64 + jj, N - 1) * D, qq, kvb);
-            score(j0, kva);
-            if (j0 + 64 >= N) break;
-            if (j0 + 128 < N) load_kbar_quarter<D>(kh + (size_t)min(j0 + 128 + jj, N - 1) * D, qq, kva);
-            score(j0 + 64, kvb);
+        for (int e = 0; e < QD / 4; ++e) {
+            const float4 t = src[e];
+            qv[4 * e] = t.x; qv[4 * e + 1] = t.y; qv[4 * e + 2] = t.z; qv[4 * e + 3] = t.w;
         }
+    }
+    const float* kh = kbar + (size_t)h * N * D;
+    const int NKT = (N + 15) / 16;
+    auto kload = [&](int kt, float (&kv)[QD]) __attribute__((always_inline)) {
+        const float4* src = reinterpret_cast<const float4*>(kh + (size_t)min(kt * 16 + l16, N - 1) * D + g * QD);
+#pragma unroll
+        for (int e = 0; e < QD / 4; ++e) {
+            const float4 t = src[e];
+            kv[4 * e] = t.x; kv[4 * e + 1] = t.y; kv[4 * e + 2] = t.z; kv[4 * e + 3] = t.w;
+        }
+    };
+    auto score = [&](int kt, const float (&kv)[QD]) __attribute__((always_inline)) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < QD; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[st], kv[st], acc, 0, 0, 0);
+        const int j = kt * 16 + l16;  // lane holds rows 4g .. 4g+3 of key j
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            if (4 * g + x < R && j < N) rows[(4 * g + x) * N + j] = acc[x] * c;
+    };
+    float kva[QD], kvb[QD];
+    if (wave < NKT) kload(wave, kva);
+#pragma unroll 1
+    for (int kt = wave; kt < NKT; kt += 8) {
+        if (kt + 4 < NKT) kload(kt + 4, kvb);
+        score(kt, kva);
+        if (kt + 4 >= NKT) break;
+        if (kt + 8 < NKT) kload(kt + 8, kva);
+        score(kt + 4, kvb);
     }
     __syncthreads();
 
@@ -322,13 +334,15 @@ template <int D>
 hipError_t route_d(const float* qbar, const float* kbar, int H, int N, float c, float beta,
                    const float* tau_in, float* tau, int32_t* kept, uint32_t* sel, int* queues,
                    int topk, hipStream_t s) {
-    // as many rows per workgroup as 64 KB of LDS holds
-    const size_t row_bytes = sizeof(float) * ((size_t)N + QbarLds<D>::SIZE);
+    // as many rows per workgroup (at most one 16-row MFMA tile) as 80 KB of
+    // LDS holds (two workgroups per CU share its 160 KB)
+    const size_t row_bytes = sizeof(float) * (size_t)N;
+    constexpr size_t kLds = 80 * 1024;
 #define SOL_ROUTE(R) route_t<D, R>(qbar, kbar, H, N, c, beta, tau_in, tau, kept, sel, queues, topk, s)
-    if (16 * row_bytes <= 65536) return SOL_ROUTE(16);
-    if (8 * row_bytes <= 65536) return SOL_ROUTE(8);
-    if (4 * row_bytes <= 65536) return SOL_ROUTE(4);
-    if (2 * row_bytes <= 65536) return SOL_ROUTE(2);
+    if (16 * row_bytes <= kLds) return SOL_ROUTE(16);
+    if (8 * row_bytes <= kLds) return SOL_ROUTE(8);
+    if (4 * row_bytes <= kLds) return SOL_ROUTE(4);
+    if (2 * row_bytes <= kLds) return SOL_ROUTE(2);
     return SOL_ROUTE(1);
 #undef SOL_ROUTE
 }

@@ -80,8 +80,9 @@ int sol_pool(const void* q, const void* k, const void* v,
  *              decisions themselves, bit (j % 32) of word j / 32 of row (h, i)
  *              set iff s_ij > tau_i (the layout of sol_attn_fwd_dbg's
  *              sel_mask).  sol_sweep can take them instead of deriving them.
- * The counts and bits are those the forward pass uses: every stage computes
- * each s_ij with the same arithmetic.
+ * The counts and bits are those the forward pass uses (the same kernel
+ * forms every s_ij, by fp32 matrix instructions; both sweeps take their
+ * decisions from these bits).
  */
 int sol_route(const float* qbar, const float* kbar, int H, int L, int d, int B,
               float beta, float* tau, int32_t* kept_counts, uint32_t* sel_bits,
@@ -98,10 +99,9 @@ int sol_route(const float* qbar, const float* kbar, int H, int L, int d, int B,
  *             256-byte aligned (scratch: work counters and bf16 copies of the
  *             pooled keys and summed values).
  * sel_bits  : DEVICE, the decisions sol_route wrote for these thresholds, or
- *             NULL.  bf16: when given, the sweep takes its decisions from
- *             them and launches no routing pass of its own; when NULL it first
- *             derives them from tau.  fp32: ignored (the fp32 kernel decides
- *             from tau itself, with the same arithmetic).
+ *             NULL.  When given, the sweep takes its decisions from them and
+ *             launches no routing pass of its own; when NULL it first derives
+ *             them from tau.
  * sel_mask  : as in sol_attn_fwd_dbg (the decisions taken), or NULL.
  */
 int sol_sweep(const void* q, const void* k, const void* v,
