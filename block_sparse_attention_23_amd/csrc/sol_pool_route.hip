@@ -150,25 +150,43 @@ __device__ __forceinline__ float order_key_value(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-__device__ void route_rows_topk(const float* rows, int N, int nr, int k, int wave, int lane,
+// count of keys >= cand in a row: from registers (kr, nch chunks of 64) or LDS
+template <bool REG, int MAXC>
+__device__ __forceinline__ int count_at_least(const float* row, const uint32_t (&kr)[MAXC], int N,
+                                              int nch, int lane, uint32_t cand) {
+    int cnt = 0;
+    if constexpr (REG) {
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c)
+            if (c < nch) cnt += __popcll(__ballot(kr[c] >= cand));
+    } else {
+        for (int j0 = 0; j0 < N; j0 += 64) {
+            const int j = j0 + lane;
+            cnt += __popcll(__ballot(j < N && order_key(row[j]) >= cand));
+        }
+    }
+    return cnt;
+}
+
+template <bool REG>
+__device__ __forceinline__ void route_rows_topk(const float* rows, int N, int nr, int k, int wave, int lane,
                                 uint32_t* sel, int W, float* tau, int32_t* kept) {
+    constexpr int MAXC = REG ? 32 : 1;  // keys held in registers: N <= 64 MAXC
+    const int nch = (N + 63) / 64;
     for (int r = wave; r < nr; r += 4) {
         const float* row = rows + r * N;
+        uint32_t kr[MAXC];  // key of block 64 c + lane (0, never counted, past N)
+#pragma unroll
+        for (int c = 0; c < MAXC; ++c) {
+            const int j = 64 * c + lane;
+            kr[c] = (REG && c < nch && j < N) ? order_key(row[j]) : 0u;
+        }
         uint32_t T = 0;  // largest key with at least k keys >= it
         for (int b = 31; b >= 0; --b) {
             const uint32_t cand = T | (1u << b);
-            int cnt = 0;
-            for (int j0 = 0; j0 < N; j0 += 64) {
-                const int j = j0 + lane;
-                cnt += __popcll(__ballot(j < N && order_key(row[j]) >= cand));
-            }
-            if (cnt >= k) T = cand;
+            if (count_at_least<REG, MAXC>(row, kr, N, nch, lane, cand) >= k) T = cand;
         }
-        int above = 0;
-        for (int j0 = 0; j0 < N; j0 += 64) {
-            const int j = j0 + lane;
-            above += __popcll(__ballot(j < N && order_key(row[j]) > T));
-        }
+        const int above = T == 0xFFFFFFFFu ? 0 : count_at_least<REG, MAXC>(row, kr, N, nch, lane, T + 1u);
         const int need = k - above;  // keys equal to T still to keep
         uint32_t* srow = sel ? sel + (size_t)r * W : nullptr;
         int seen = 0, cnt = 0;
@@ -256,8 +274,13 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
     __syncthreads();
 
     if (topk >= 0) {
-        route_rows_topk(rows, N, nr, topk, wave, lane, sel ? sel + ((size_t)h * N + i0) * W : nullptr,
-                        W, tau_out + (size_t)h * N + i0, kept + (size_t)h * N + i0);
+        uint32_t* srows = sel ? sel + ((size_t)h * N + i0) * W : nullptr;
+        if (N <= 64 * 32)
+            route_rows_topk<true>(rows, N, nr, topk, wave, lane, srows, W, tau_out + (size_t)h * N + i0,
+                                  kept + (size_t)h * N + i0);
+        else
+            route_rows_topk<false>(rows, N, nr, topk, wave, lane, srows, W, tau_out + (size_t)h * N + i0,
+                                   kept + (size_t)h * N + i0);
         return;
     }
     // statistics: wave w handles rows w, w+4, ... (lane-strided sums in a
