@@ -53,14 +53,18 @@ def parse():
     return ap.parse_args()
 
 
+SWEEP_SOURCES = ("sol_device.h", "sol_launch.h", "sol_sweep.hip")
+
+
 def source_digest():
-    """Digest of the kernel sources' code: comments and whitespace are
-    dropped first, so a comment edit keeps recorded counters valid."""
+    """Digest of the code the sweep kernel is built from (its source and the
+    headers it includes): comments and whitespace are dropped first, so a
+    comment edit keeps recorded counters valid."""
     import hashlib
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_sparse_attention_23_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in SWEEP_SOURCES:
         with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             code = fh.read()
         code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
