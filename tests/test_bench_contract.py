@@ -1,0 +1,33 @@
+"""bench.py's command-line contract, checked on the CPU: it runs on one GPU
+only and says so for --gpus N > 1, before touching a GPU."""
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def run_bench(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                          capture_output=True, text=True, timeout=120, cwd=ROOT)
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = run_bench("--gpus", "2", "--steps", "1", "--warmup", "0")
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""
+
+
+def test_options_parse():
+    sys.path.insert(0, ROOT)
+    import bench
+    old = sys.argv
+    try:
+        sys.argv = ["bench.py", "--workload", "C6", "--betas", "1.25,1.5", "--steps", "3",
+                    "--warmup", "1", "--no-dense", "--no-cpu-baseline", "--ablation"]
+        a = bench.parse()
+    finally:
+        sys.argv = old
+    assert (a.workload, a.betas, a.steps, a.warmup, a.no_dense, a.no_cpu_baseline, a.ablation) == \
+        ("C6", "1.25,1.5", 3, 1, True, True, True)
