@@ -65,8 +65,14 @@ struct Sweep {
     // LDS layout of the K (or V) rows of a tile: NB blocks of 1 KB plus
     // padding; key k is row k / NB of block k % NB.
     static constexpr int NB = 64 * 2 * D / 1024;        // blocks per tile half
-    static constexpr int KPAD = 16, VPAD = 16;           // padding per block (elements)
-    static constexpr int KSLOT = NB * (512 + KPAD);      // elements of a K buffer
+    static constexpr int VPAD = 16;                      // V padding per block (elements)
+    // first element of K block b: 1 KB per block plus 32 bytes per block at
+    // d = 128; at d = 64 the eight blocks start 0, 32, 64, 96, 256, 288, 320,
+    // 352 bytes past their 1 KB boundaries
+    static constexpr __host__ __device__ int kbase(int b) {
+        return 512 * b + (D >= 128 ? 16 * b : 16 * (b & 3) + 128 * (b >> 2));
+    }
+    static constexpr int KSLOT = kbase(NB);              // elements of a K buffer
     static constexpr int VSLOT = NB * (512 + VPAD);      // elements of a V buffer
 };
 
@@ -77,13 +83,14 @@ constexpr uint32_t kIndexMask = (1u << kPartShift) - 1u;
 // LDS layout of the K rows (or V rows) of a tile, chosen so that the reads
 // below avoid bank conflicts and every part of a read address other than
 // the lane's own offset is an instruction immediate: key k sits in row k / NB
-// of 1 KB block k % NB, and the blocks are padded by 32 bytes.  Measured on
-// gfx950 (bank-conflict counters on these exact patterns), the LDS behaves
-// as 128 four-byte banks with a 16-byte read served 32 lanes at a time: at
-// d = 128 the 32 lanes of a K read then cover all 128 banks once, and the
-// transposing V reads are conflict-free at d = 64 and d = 128 (at d = 64 a
-// K read still meets one conflict in four cycles: no uniform padding of the
-// eight 1 KB blocks avoids it).
+// of 1 KB block k % NB.  Measured on gfx950 (bank-conflict counters on these
+// exact patterns), the LDS behaves as 128 four-byte banks with a 16-byte read
+// served 32 lanes at a time.  V blocks are padded by 32 bytes, which keeps
+// the transposing V reads conflict-free at d = 64 and d = 128.  K block b
+// starts kbase(b) elements in: 32 bytes of padding per block at d = 128;
+// at d = 64, where a uniform padding cannot work, the offsets put the first
+// banks of the eight blocks at 0, 8, 16, 24, 64, 72, 80 and 88, so the 32
+// lanes of a K read (8 blocks x 2 rows x 2 chunks) cover all 128 banks.
 
 // Direct-to-LDS loads of a tile: load i of wave w fills block b = w*LPT + i
 // of the K (and of the V) buffer -- lane l writes bytes 16 l .. 16 l + 15 of
@@ -145,7 +152,7 @@ __device__ __forceinline__ void tile_issue(const TileSrc& src, u16* Kdst, u16* V
 #if defined(__HIP_DEVICE_COMPILE__)
         const int b = wave_s * S::LPT + I;
         const uint32_t off = lane_base + 2u * D * I;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, (lds_void_t*)(Kdst + b * (512 + S::KPAD)), 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, (lds_void_t*)(Kdst + S::kbase(b)), 16, off, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(src.v, (lds_void_t*)(Vdst + b * (512 + S::VPAD)), 16, off, 0, 0, 0);
 #endif
         tile_issue<D, BLK, I + 1, IEND>(src, Kdst, Vdst, wave_s, lane_base);
@@ -189,7 +196,7 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
     // K: key l16 of a 16-key tile, 16-byte chunk g of a 32-deep step.  V: the
     // transposing read of key 4g + (l16 >> 2) of a 16-key group, columns
     // 8 ((l16 & 3) >> 1) + 4 (l16 & 1) of a 16-wide d tile.
-    const int k_lane = (l16 % S::NB) * (512 + S::KPAD) + (l16 / S::NB) * D + 8 * g;
+    const int k_lane = S::kbase(l16 % S::NB) + (l16 / S::NB) * D + 8 * g;
     const int k4 = 4 * g + (l16 >> 2), tp = l16 & 3;
     const int v_lane = (k4 % S::NB) * (512 + S::VPAD) + (k4 / S::NB) * D + 8 * (tp >> 1) + 4 * (tp & 1);
 
