@@ -11,7 +11,7 @@ import oracle
 from block_sparse_attention_23_amd import binding
 from block_sparse_attention_23_amd import inputs as gen
 
-from .parity import TOL, judge_output, run_and_check, to_device
+from .parity import TOL, block_rows, judge_output, run_and_check, to_device
 
 pytestmark = pytest.mark.gpu
 INF = math.inf
@@ -164,3 +164,17 @@ def test_stage_entry_points_equal_forward(dtype, d, B, L):
     for m in (bits, mask_a, mask_b):
         assert torch.equal(m, sel_f)
     assert torch.equal(out_a, out_f) and torch.equal(out_b, out_f)
+
+
+def test_largest_supported_block_count():
+    """N = 8192 key blocks (the library's bound), ragged last block: the
+    routing kernel's fewest rows per workgroup and the sweep's largest tile
+    list.  Selection over every (i, j); outputs on sampled query blocks."""
+    L = 8192 * 64 - 37
+    inp = gen.grid_inputs(1, (8, 64, 1024), 64, 21, "bf16", truncate=L)
+    N = -(-L // 64)
+    assert N == 8192
+    blocks = [0, 1, N // 2, N - 1]
+    rows = block_rows(L, 64, [(0, i) for i in blocks])
+    s = run_and_check(inp, 64, 1.0, rows=rows)
+    print(f"N=8192: kept={s['kept_frac']:.4f} flips={s['flips']} max_err={s['max_err']:.2e}", flush=True)
