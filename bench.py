@@ -208,8 +208,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); use --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(heads shard across GPUs with no exchange); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

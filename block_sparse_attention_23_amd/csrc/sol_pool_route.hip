@@ -1,6 +1,7 @@
 // sol_pool_route.hip -- the two stages before the sweep ("Sol-Attn" visual
 // explainer, "The complete idea in one pass": pool Q, K and V into blocks;
-// the threshold-computation stage before the proxy-score stream).
+// computing the thresholds, which its overview places ahead of the stream of
+// proxy scores).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -135,7 +136,8 @@ __global__ void __launch_bounds__(256) pooled_to_bf16_kernel(const float* __rest
 // sweeps read: the routing kernel is the one place s_ij is formed.
 // ============================================================================
 // Fixed-budget selection, the comparator the abstract contrasts Sol-Attn
-// with (a fixed fraction of top-ranked blocks by proxy score): each of the
+// with (every query block keeps the same share of key blocks, the highest
+// proxy scores first): each of the
 // nr rows keeps its k largest scores, ties to the lower block index.  Wave
 // w ranks rows w, w + 4, ... held in LDS: the k-th largest score is found
 // exactly by a binary search over order-preserving 32-bit keys (counts from

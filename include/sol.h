@@ -153,11 +153,11 @@ int sol_attn_fwd_dbg(const void* q, const void* k, const void* v,
 
 /*
  * The forward pass with the comparators the pages contrast Sol-Attn with,
- * for accuracy studies (abstract: "selecting a fixed fraction of top-ranked
- * blocks by proxy score imposes fixed budgets" and "lossy keep-or-drop
- * sparsification"; visual explainer, "Place it among nearby methods":
- * ordinary block sparse attention lets every unselected block contribute
- * zero).  flags is a bitwise OR of:
+ * for accuracy studies (abstract: routing that gives every query block the
+ * same share of top-scoring key blocks, and keep-or-drop sparsification that
+ * discards what is not selected; visual explainer, "Place it among nearby
+ * methods": ordinary block sparse attention lets every unselected block
+ * contribute zero).  flags is a bitwise OR of:
  *   SOL_DROP_APPROX  unselected blocks contribute nothing (no Eq. (9) /
  *                    Eq. (10) approximate terms); a row whose selection is
  *                    empty is written as zeros.

@@ -226,8 +226,9 @@ int sol_oracle_moments(const double* qbar, const double* kbar,
 }
 
 /*
- * Fixed-budget comparator ([ABS]: selecting a fixed fraction of top-ranked
- * blocks by proxy score imposes fixed budgets): every query block keeps the
+ * Fixed-budget comparator ([ABS]: the routing the abstract contrasts with,
+ * one share of key blocks for every query block, ranked by proxy score):
+ * every query block keeps the
  * k key blocks with the largest proxy scores s_ij = c * qbar_i . kbar_j (the
  * same proxy as sol_oracle_route), k the same for every (h, i).  Ties in the
  * score go to the lower block index (the pages do not say).
@@ -313,7 +314,7 @@ int sol_oracle_route_topk(const double* qbar, const double* kbar, int H, int N, 
  *
  * drop_approx != 0 gives the keep-or-drop scheme the pages contrast with
  * ([VE] "Place it among nearby methods", ordinary block sparse attention:
- * every unselected block contributes zero; [ABS] "lossy keep-or-drop"): the
+ * every unselected block contributes zero; [ABS] keep-or-drop): the
  * terms over U_i are left out of both sums, and a row whose S_i is empty
  * (D_r = 0) is set to zero (the pages do not say).
  */
