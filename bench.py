@@ -325,7 +325,8 @@ def main():
         "exact_tile_mfma_util": head["F_exact"] / (st["sweep"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": traffic, "kernel": "sweep_bf16_kernel<128, 64, false>",
+                     "traffic": traffic, "kernel": (f"sweep_bf16_kernel<{d}, {B}, false>" if w.dtype == "bf16"
+                                                    else f"attn_f32_kernel<{d}, {B}, false>"),
                      "algorithmic_flop_per_launch": F_alg},
         "stage_ms": st,
         "pool_gbs": pool_bytes / (st["pool"] * 1e-3) / 1e9,

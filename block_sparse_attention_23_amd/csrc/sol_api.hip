@@ -22,7 +22,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 int check_shape(int H, int L, int d, int B) {
     if (H < 1 || L < 1 || d < 1 || B < 1) return SOL_EINVAL;
     if (d != 64 && d != 128) return SOL_EUNSUPPORTED;
-    if (B != 64 && B != 128) return SOL_EUNSUPPORTED;
+    if (B != 32 && B != 64 && B != 128) return SOL_EUNSUPPORTED;
     const long long N = ((long long)L + B - 1) / B;
     if (N > kMaxBlocks) return SOL_EUNSUPPORTED;
     if ((long long)H * N > (1LL << 30)) return SOL_EUNSUPPORTED;
@@ -275,7 +275,7 @@ const char* sol_status_string(int status) {
     switch (status) {
         case SOL_OK: return "success";
         case SOL_EINVAL: return "invalid argument (null or misaligned pointer, bad size, NaN beta or bad dtype)";
-        case SOL_EUNSUPPORTED: return "unsupported shape (d and B must be 64 or 128; N <= 8192)";
+        case SOL_EUNSUPPORTED: return "unsupported shape (d must be 64 or 128, B 32, 64 or 128; N <= 8192)";
         case SOL_EWORKSPACE: return "workspace missing, misaligned or smaller than sol_workspace_bytes()";
         case SOL_EHIP: return "HIP kernel launch failed";
         default: return "unknown status";

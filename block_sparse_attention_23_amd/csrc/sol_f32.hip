@@ -139,9 +139,9 @@ __global__ void __launch_bounds__(4 * BLK) attn_f32_kernel(AttnArgs a) {
                 __syncthreads();
                 if (wave == 0) {
                     int base = 0;
-                    for (int hh = 0; hh < BLK / 64; ++hh) {
+                    for (int hh = 0; hh < (BLK + 63) / 64; ++hh) {
                         const int jj = hh * 64 + lane;
-                        const bool sel = flag_s[jj] == 1;
+                        const bool sel = jj < BLK && flag_s[jj] == 1;
                         const uint64_t msk = __ballot(sel);
                         const int pos = base + __popcll(msk & ((1ull << lane) - 1ull));
                         if (sel) sel_list[pos] = j0 + jj;
@@ -215,6 +215,8 @@ hipError_t f32_t(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_attn_f32(const AttnArgs& a, int d, int B, bool dense, hipStream_t s) {
+    if (d == 64 && B == 32 && !dense) return f32_t<64, 32, false>(a, s);
+    if (d == 128 && B == 32 && !dense) return f32_t<128, 32, false>(a, s);
     if (d == 64 && B == 64) return dense ? f32_t<64, 64, true>(a, s) : f32_t<64, 64, false>(a, s);
     if (d == 64 && B == 128) return dense ? f32_t<64, 128, true>(a, s) : f32_t<64, 128, false>(a, s);
     if (d == 128 && B == 64) return dense ? f32_t<128, 64, true>(a, s) : f32_t<128, 64, false>(a, s);

@@ -378,6 +378,8 @@ hipError_t launch_pool(const void* q, const void* k, const void* v, int bf16, in
                        int B, float* qbar, float* kbar, float* vsum, u16* kbar_bf, u16* vsum_bf,
                        hipStream_t s) {
     const int N = (L + B - 1) / B;
+    if (d == 64 && B == 32) return pool_t<64, 32>(q, k, v, bf16, H, L, N, qbar, kbar, vsum, kbar_bf, vsum_bf, s);
+    if (d == 128 && B == 32) return pool_t<128, 32>(q, k, v, bf16, H, L, N, qbar, kbar, vsum, kbar_bf, vsum_bf, s);
     if (d == 64 && B == 64) return pool_t<64, 64>(q, k, v, bf16, H, L, N, qbar, kbar, vsum, kbar_bf, vsum_bf, s);
     if (d == 64 && B == 128) return pool_t<64, 128>(q, k, v, bf16, H, L, N, qbar, kbar, vsum, kbar_bf, vsum_bf, s);
     if (d == 128 && B == 64) return pool_t<128, 64>(q, k, v, bf16, H, L, N, qbar, kbar, vsum, kbar_bf, vsum_bf, s);

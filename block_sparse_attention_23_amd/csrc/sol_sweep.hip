@@ -1,18 +1,20 @@
 // sol_sweep.hip -- the fused Sol-Attn sweep for bf16 inputs on gfx950.
 //
-// A workgroup (4 waves) owns 128 query rows at a time: two 64-row query
-// blocks (B = 64) or one 128-row block (B = 128).  Wave w owns rows
-// 32w .. 32w+31 as two 16-row tiles of v_mfma_f32_16x16x32_bf16.
+// A workgroup (4 waves) owns 128 query rows at a time: four 32-row query
+// blocks (B = 32), two 64-row blocks (B = 64) or one 128-row block
+// (B = 128).  Wave w owns rows 32w .. 32w+31 as two 16-row tiles of
+// v_mfma_f32_16x16x32_bf16.
 //
 // Per workgroup ("Sol-Attn" visual explainer, "The complete idea in one
 // pass", Eq. (4), Eq. (9), Eq. (10), Eq. (11)):
 //   1. the tile list: the routing kernel's selection bits of the two query
 //      blocks (bit j of block i is s_ij > tau_i) are copied to LDS; a tile
-//      list follows: one approximate entry per chunk of B pooled keys that
-//      holds an unselected block of either query block, then one exact entry
-//      per key block that either query block selected (the union, so a key
-//      block chosen by both is loaded once), each tagged with the query
-//      blocks that use it.
+//      list follows: one approximate entry per chunk of max(B, 64) pooled
+//      keys that holds an unselected block of a query block, then one exact
+//      entry per key block that a query block selected (the union, so a key
+//      block chosen by several is loaded once; at B = 32, per aligned pair of
+//      key blocks 2j, 2j+1, one 64-key tile), each tagged with the query
+//      blocks that use it (at B = 32, per key block of the pair).
 //   2. the tile loop over 64-key tiles.  Tiles stream from HBM straight into
 //      LDS (direct-to-LDS buffer loads, 16 bytes a lane) into two buffers, so
 //      the next tile loads while the current one is computed; the loads are
@@ -55,7 +57,14 @@ template <int D, int BLK>
 struct Sweep {
     static constexpr int NT = 256;                      // 4 waves
     static constexpr int QB = 128 / BLK;                // query blocks per workgroup
-    static constexpr int SUB = BLK / 64;                // 64-key tiles per key block
+    static constexpr int TB = BLK < 64 ? 64 : BLK;      // tokens (or pooled keys) per tile-list entry
+    static constexpr int SUB = TB / 64;                 // 64-key tiles per entry
+    static constexpr int KPT = BLK < 64 ? 64 / BLK : 1;  // key blocks per exact 64-key tile (2 at B = 32)
+    // tile-list entry: bit 31 approximate; bits PS .. 30 the query blocks
+    // that use it (exact entries at B = 32: bit h QB + b for key block 2j + h
+    // of the pair); bits 0 .. PS-1 the chunk, key block or pair index
+    static constexpr int PB = QB * KPT < 2 ? 2 : QB * KPT;
+    static constexpr int PS = 31 - PB;
     static constexpr int CH = D / 8;                    // 16-byte chunks per row
     static constexpr int RPK = 1024 / (2 * D);          // rows per 1 KB of LDS
     static constexpr int LPT = (64 * D * 2) / (NT * 16);  // direct loads per thread per tile
@@ -77,8 +86,6 @@ struct Sweep {
 };
 
 constexpr uint32_t kApprox = 0x80000000u;  // tile-list entry: approximate chunk
-constexpr int kPartShift = 29;             // bits 29..30: query blocks using the entry
-constexpr uint32_t kIndexMask = (1u << kPartShift) - 1u;
 
 // LDS layout of the K rows (or V rows) of a tile, chosen so that the reads
 // below avoid bank conflicts and every part of a read address other than
@@ -179,11 +186,11 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform within a wave
     const int l16 = lane & 15, g = lane >> 4;
     const int H = a.H, L = a.L, N = a.N;
-    const int NC = (N + BLK - 1) / BLK;
+    const int NC = (N + S::TB - 1) / S::TB;  // approximate chunks
     const int nwords = (N + 31) / 32;
     const int NG = (N + S::QB - 1) / S::QB;  // 128-row groups per head
     uint32_t* selbits = dyn;                 // [QB][nwords]
-    uint32_t* tiles = dyn + S::QB * nwords;  // up to NC + N entries
+    uint32_t* tiles = dyn + S::QB * nwords;  // up to NC + ceil(N / KPT) entries
     const int myb = (wave * 32) / BLK;       // this wave's query block within the group
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t dma_base = dma_lane_base<D, BLK>(wave_s, lane);
@@ -262,11 +269,11 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                     const int c = c0 + lane;
                     uint32_t part = 0;
                     if (c < NC) {
-                        const int lo = c * BLK, cnt = min(BLK, N - lo);
+                        const int lo = c * S::TB, cnt = min(S::TB, N - lo);
                         for (int b = 0; b < nqb; ++b) {
                             int ones = 0;
 #pragma unroll
-                            for (int w32 = 0; w32 < BLK / 32; ++w32) {
+                            for (int w32 = 0; w32 < S::TB / 32; ++w32) {
                                 const int bit0 = lo + 32 * w32;
                                 if (bit0 < N) {
                                     uint32_t wd = selbits[b * nwords + (bit0 >> 5)];
@@ -279,18 +286,23 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                         }
                     }
                     const uint64_t m = __ballot(part != 0);
-                    if (part) tiles[nt + __popcll(m & ((1ull << lane) - 1ull))] = kApprox | (part << kPartShift) | c;
+                    if (part) tiles[nt + __popcll(m & ((1ull << lane) - 1ull))] = kApprox | (part << S::PS) | c;
                     nt += __popcll(m);
                 }
-                // exact key blocks, ascending
-                for (int j0 = 0; j0 < N; j0 += 64) {
-                    const int j = j0 + lane;
+                // exact key blocks (pairs of key blocks at B = 32), ascending
+                const int NE = (N + S::KPT - 1) / S::KPT;
+                for (int j0 = 0; j0 < NE; j0 += 64) {
+                    const int je = j0 + lane;
                     uint32_t part = 0;
-                    if (j < N)
-                        for (int b = 0; b < nqb; ++b)
-                            part |= ((selbits[b * nwords + (j >> 5)] >> (j & 31)) & 1u) << b;
+#pragma unroll
+                    for (int hk = 0; hk < S::KPT; ++hk) {
+                        const int j = je * S::KPT + hk;
+                        if (je < NE && j < N)
+                            for (int b = 0; b < nqb; ++b)
+                                part |= ((selbits[b * nwords + (j >> 5)] >> (j & 31)) & 1u) << (hk * S::QB + b);
+                    }
                     const uint64_t m = __ballot(part != 0);
-                    if (part) tiles[nt + __popcll(m & ((1ull << lane) - 1ull))] = (part << kPartShift) | j;
+                    if (part) tiles[nt + __popcll(m & ((1ull << lane) - 1ull))] = (part << S::PS) | je;
                     nt += __popcll(m);
                 }
                 if (lane == 0) misc_s[1] = nt;
@@ -329,14 +341,14 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
         // itself, the same for the whole workgroup (kept scalar).
         auto word_raw = [&](int t) -> uint32_t { return DENSE ? 0u : tiles[t / S::SUB]; };
         auto word_of = [&](int t, uint32_t raw) -> uint32_t {
-            return DENSE ? ((all_part << kPartShift) | (uint32_t)(t / S::SUB))
+            return DENSE ? ((all_part << S::PS) | (uint32_t)(t / S::SUB))
                          : (uint32_t)__builtin_amdgcn_readfirstlane((int)raw);
         };
         // (approx?, part, row0 of the tile in its source) of tile t
         auto decode = [&](uint32_t d, int t, bool& approx, uint32_t& part, int& row0) {
             approx = (d & kApprox) != 0;
-            part = (d >> kPartShift) & 3u;
-            row0 = (int)(d & kIndexMask) * BLK + (t % S::SUB) * 64;
+            part = (d >> S::PS) & ((1u << S::PB) - 1u);
+            row0 = (int)(d & ((1u << S::PS) - 1u)) * S::TB + (t % S::SUB) * 64;
         };
         auto source_of = [&](uint32_t d, int t) {
             bool ap;
@@ -361,9 +373,10 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             uint32_t part;
             int row0;
             decode(w_t, t, approx, part, row0);
-            const bool mine = (part >> myb) & 1u;  // this wave's query block uses tile t
+            // this wave's query block uses tile t (at B = 32: one of its key blocks)
+            const bool mine = ((part >> myb) | (S::KPT == 2 && !approx ? part >> (S::QB + myb) : 0u)) & 1u;
             if (t + 1 < TS) {  // tile t+1 streams into (Kn, Vn)
-                if (S::QB == 1 || part == 3u)
+                if (S::QB != 2 || part == 3u)
                     tile_issue<D, BLK>(source_of(w_t1, t + 1), Kn, Vn, wave_s, dma_base);
                 else if (!mine)
                     tile_issue<D, BLK, 0, 2 * S::LPT>(source_of(w_t1, t + 1), Kn, Vn, 2 * (wave_s & 1),
@@ -403,10 +416,13 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             }
 
             // column masks: tokens past L (exact), selected or past-N pooled
-            // keys (approximate).  Lane key jj = 16 kt + 4g + r is bit
-            // 16 kt + r of colsel >> 4g.
+            // keys (approximate), and at B = 32 the key block of a pair that
+            // this wave's query block did not select (exact).  Lane key
+            // jj = 16 kt + 4g + r is bit 16 kt + r of colsel >> 4g.
             const int limit = approx ? N : L;
-            if (approx || row0 + 64 > limit) {
+            // bit h: this wave's query block uses key block h of the pair
+            const uint32_t halves = S::KPT == 2 && !approx ? ((part >> myb) & 1u) | (((part >> (S::QB + myb)) & 1u) << 1) : 3u;
+            if (approx || row0 + 64 > limit || halves != 3u) {
                 uint64_t colsel = 0;
                 if (approx) {
                     const uint32_t* sb = selbits + myb * nwords;
@@ -422,7 +438,7 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                     for (int r = 0; r < 4; ++r) {
                         const int bit = kt * 16 + r;
                         const uint32_t w = bit < 32 ? cs_lo : cs_hi;
-                        const bool valid = g4 < lim - bit && !((w >> (bit & 31)) & 1u);
+                        const bool valid = g4 < lim - bit && !((w >> (bit & 31)) & 1u) && ((halves >> (kt >> 1)) & 1u);
                         if (!valid) sacc[kt][0][r] = sacc[kt][1][r] = -INFINITY;
                     }
             }
@@ -591,8 +607,11 @@ template <int D, int BLK, bool DENSE>
 hipError_t sweep_t(const AttnArgs& a, hipStream_t s) {
     using S = Sweep<D, BLK>;
     auto kern = sweep_bf16_kernel<D, BLK, DENSE>;
-    const int NC = (a.N + BLK - 1) / BLK;
-    const size_t dyn = DENSE ? 0 : sizeof(uint32_t) * ((size_t)S::QB * ((a.N + 31) / 32) + NC + a.N);
+    const int NC = (a.N + S::TB - 1) / S::TB;
+    // selection bits of the group's query blocks, then at most NC approximate
+    // and ceil(N / KPT) exact tile-list entries
+    const size_t dyn = DENSE ? 0 : sizeof(uint32_t) * ((size_t)S::QB * ((a.N + 31) / 32) + NC +
+                                                       (a.N + S::KPT - 1) / S::KPT);
     int grid;
     if (DENSE) {
         const int NG = (a.N + S::QB - 1) / S::QB;
@@ -611,6 +630,9 @@ hipError_t sweep_t(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_sweep_bf16(const AttnArgs& a, int d, int B, bool dense, hipStream_t s) {
+    // (the dense kernel runs with B = 64 only)
+    if (d == 64 && B == 32 && !dense) return sweep_t<64, 32, false>(a, s);
+    if (d == 128 && B == 32 && !dense) return sweep_t<128, 32, false>(a, s);
     if (d == 64 && B == 64) return dense ? sweep_t<64, 64, true>(a, s) : sweep_t<64, 64, false>(a, s);
     if (d == 64 && B == 128) return dense ? sweep_t<64, 128, true>(a, s) : sweep_t<64, 128, false>(a, s);
     if (d == 128 && B == 64) return dense ? sweep_t<128, 64, true>(a, s) : sweep_t<128, 64, false>(a, s);

@@ -96,6 +96,13 @@ WORKLOADS = {
                    grids=((32, 64, 64),), headline_beta=1.25,
                    desc="long-sequence kernel point: 24 heads, 32x64x64 grid, L=131072, d=128, "
                         "B=64, bf16"),
+    # The same inputs at B = 32, the smallest block size the pages' integration
+    # notes suggest sweeping (papers.ananclaw.com explainer, its integration
+    # notes: try 32, 64 and 128 on the target hardware).
+    "C6b": Workload("C6b", H=24, d=128, B=32, dtype="bf16", betas=(1.0, 1.25, 1.5), seed=5,
+                    grids=((32, 64, 64),), headline_beta=1.25,
+                    desc="long-sequence kernel point at B=32: 24 heads, 32x64x64 grid, L=131072, "
+                         "d=128, B=32, bf16"),
 }
 
 

@@ -21,7 +21,7 @@
  *    caller's next synchronisation of the stream.
  *  - Return value: SOL_OK, or a negative sol_status_t.  Argument errors are
  *    detected before anything is enqueued, and nothing is written then.
- *  - Supported shapes: d in {64, 128}, B in {64, 128}, H >= 1, 1 <= L and
+ *  - Supported shapes: d in {64, 128}, B in {32, 64, 128}, H >= 1, 1 <= L and
  *    N <= 8192; anything else returns SOL_EUNSUPPORTED.
  *  - Calls that share a workspace must be ordered on one stream; concurrent
  *    calls need distinct workspaces.

@@ -56,8 +56,9 @@ def test_workspace_bytes(lib):
     assert n >= 3 * H * N * d * 4 + H * N * 4
     assert n % 256 == 0
     assert binding.workspace_bytes(1, 1, 64, 64) > 0
-    for bad in [(0, 10, 64, 64), (1, 0, 64, 64), (1, 10, 96, 64), (1, 10, 64, 32),
-                (1, 8192 * 64 + 1, 64, 64)]:
+    assert binding.workspace_bytes(1, 8192 * 32, 128, 32) > 0
+    for bad in [(0, 10, 64, 64), (1, 0, 64, 64), (1, 10, 96, 64), (1, 10, 64, 16),
+                (1, 8192 * 64 + 1, 64, 64), (1, 8192 * 32 + 1, 64, 32)]:
         assert binding.workspace_bytes(*bad) == 0
 
 
@@ -76,7 +77,8 @@ def test_forward_rejects_bad_arguments_before_launch(lib):
     assert _fwd(lib, H=0) == -1
     assert _fwd(lib, L=-5) == -1
     assert _fwd(lib, d=96) == -2
-    assert _fwd(lib, B=32) == -2
+    assert _fwd(lib, B=16) == -2
+    assert _fwd(lib, B=96) == -2
     assert _fwd(lib, L=8192 * 64 + 1) == -2
     assert _fwd(lib, beta=math.nan) == -1
     assert _fwd(lib, dt=5) == -1

@@ -32,7 +32,8 @@ def grid_inp(H, L, d, dtype, seed=0):
 @pytest.mark.parametrize("dtype,d,B,L", [("bf16", 128, 64, 1000), ("bf16", 64, 128, 1000),
                                          ("fp32", 64, 64, 1024), ("bf16", 128, 128, 300),
                                          ("bf16", 64, 64, 1), ("fp32", 128, 64, 77),
-                                         ("bf16", 128, 64, 4096)])
+                                         ("bf16", 128, 64, 4096), ("bf16", 128, 32, 1000),
+                                         ("fp32", 64, 32, 77)])
 def test_pool_matches_oracle(dtype, d, B, L):
     inp = grid_inp(3, L, d, dtype, seed=1)
     q, k, v = to_device(inp)
@@ -44,7 +45,7 @@ def test_pool_matches_oracle(dtype, d, B, L):
 
 
 @pytest.mark.parametrize("beta", [-INF, 0.0, 1.0, INF])
-@pytest.mark.parametrize("d,B", [(128, 64), (64, 64), (128, 128), (64, 128)])
+@pytest.mark.parametrize("d,B", [(128, 64), (64, 64), (128, 128), (64, 128), (128, 32), (64, 32)])
 @pytest.mark.parametrize("L", [1000, 1024, 130, 50, 1])
 def test_forward_bf16_small(L, d, B, beta):
     inp = grid_inp(2, L, d, "bf16", seed=L + d + B)
@@ -62,10 +63,21 @@ def test_forward_bf16_unstructured(beta):
 
 
 @pytest.mark.parametrize("beta", [-INF, 0.0, 1.0, INF])
-@pytest.mark.parametrize("d,B,L", [(64, 64, 1024), (128, 64, 333), (64, 128, 1000)])
+@pytest.mark.parametrize("d,B,L", [(64, 64, 1024), (128, 64, 333), (64, 128, 1000), (128, 32, 1000),
+                                   (64, 32, 333)])
 def test_forward_fp32(d, B, L, beta):
     inp = grid_inp(2, L, d, "fp32", seed=5)
     run_and_check(inp, B, beta)
+
+
+@pytest.mark.parametrize("beta", [0.0, 1.0, 2.0])
+def test_forward_b32_many_groups(beta):
+    """B = 32: four query blocks per workgroup and exact tiles made of aligned
+    pairs of key blocks, each half used by its own set of query blocks; 2 heads
+    of 8229 tokens (N = 258 blocks, 65 groups, ragged last block of 5 tokens)."""
+    inp = grid_inp(2, 8229, 128, "bf16", seed=12)
+    s = run_and_check(inp, 32, beta)
+    assert 0.0 < s["kept_frac"] < 1.0
 
 
 def test_forward_c1_full():

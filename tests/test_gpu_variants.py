@@ -67,7 +67,7 @@ def run_variant(inp, B, beta, keep_frac, drop, topk, rows=None):
     return stats, out
 
 
-@pytest.mark.parametrize("d,B,L", [(128, 64, 1000), (64, 128, 700), (128, 64, 130)])
+@pytest.mark.parametrize("d,B,L", [(128, 64, 1000), (64, 128, 700), (128, 64, 130), (128, 32, 1000)])
 @pytest.mark.parametrize("drop,topk", [(True, False), (False, True), (True, True)])
 def test_variants_small(d, B, L, drop, topk):
     inp = grid_inp(2, L, d, seed=12)

@@ -27,7 +27,7 @@ def workload_inputs(name):
     return _CACHE[name]
 
 
-CASES = [(n, b) for n in ("C2", "C3", "C4", "C5", "C5b", "C6") for b in gen.WORKLOADS[n].betas]
+CASES = [(n, b) for n in ("C2", "C3", "C4", "C5", "C5b", "C6", "C6b") for b in gen.WORKLOADS[n].betas]
 
 
 @pytest.mark.parametrize("name,beta", CASES, ids=[f"{n}-beta{b}" for n, b in CASES])

@@ -17,6 +17,7 @@ def test_workload_shapes():
     assert (W["C5"].L, W["C5"].N, W["C5"].L - (W["C5"].N - 1) * 128) == (65520, 512, 112)
     assert (W["C5b"].L, W["C5b"].N, W["C5b"].L - (W["C5b"].N - 1) * 128) == (65500, 512, 92)
     assert (W["C6"].L, W["C6"].N, W["C6"].L - (W["C6"].N - 1) * 64) == (131072, 2048, 64)
+    assert (W["C6b"].L, W["C6b"].N, W["C6b"].B) == (131072, 4096, 32)
     assert abs(W["C3"].dense_flops / 1e12 - 117.05) < 0.01
 
 
