@@ -178,15 +178,47 @@ def test_stage_entry_points_equal_forward(dtype, d, B, L):
     assert torch.equal(out_a, out_f) and torch.equal(out_b, out_f)
 
 
-def test_largest_supported_block_count():
+@pytest.mark.parametrize("B", [64, 32])
+def test_largest_supported_block_count(B):
     """N = 8192 key blocks (the library's bound), ragged last block: the
     routing kernel's fewest rows per workgroup and the sweep's largest tile
-    list.  Selection over every (i, j); outputs on sampled query blocks."""
-    L = 8192 * 64 - 37
+    list (at B = 32 also its largest LDS footprint).  Selection over every
+    (i, j); outputs on sampled query blocks."""
+    L = 8192 * B - (37 if B == 64 else 11)  # last block: 27 or 21 tokens
     inp = gen.grid_inputs(1, (8, 64, 1024), 64, 21, "bf16", truncate=L)
-    N = -(-L // 64)
+    N = -(-L // B)
     assert N == 8192
-    blocks = [0, 1, N // 2, N - 1]
-    rows = block_rows(L, 64, [(0, i) for i in blocks])
-    s = run_and_check(inp, 64, 1.0, rows=rows)
-    print(f"N=8192: kept={s['kept_frac']:.4f} flips={s['flips']} max_err={s['max_err']:.2e}", flush=True)
+    blocks = [0, 1, 2, 3, N // 2, N - 1]
+    rows = block_rows(L, B, [(0, i) for i in blocks])
+    s = run_and_check(inp, B, 1.0, rows=rows)
+    print(f"B={B} N=8192: kept={s['kept_frac']:.4f} flips={s['flips']} max_err={s['max_err']:.2e}",
+          flush=True)
+
+
+def test_side_stream_matches_default_stream():
+    """Every entry point runs on the stream it is given: the staged calls and
+    the fused forward on a second stream (default priority) reproduce the
+    default-stream results bit for bit, with only that stream synchronised."""
+    inp = grid_inp(2, 1500, 128, "bf16", seed=14)
+    q, k, v = to_device(inp)
+    torch.cuda.synchronize()
+    ref_out, ref_kept = binding.attn_fwd(q, k, v, 64, 1.0)
+    ref_dense = binding.attn_dense(q, k, v)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        out = torch.empty_like(q)
+        kept = torch.empty_like(ref_kept)
+        dense = torch.empty_like(q)
+        ws = binding.alloc_workspace(2, 1500, 128, 64, q.device)
+    side.synchronize()
+    binding.attn_fwd(q, k, v, 64, 1.0, out=out, kept=kept, workspace=ws, stream=side)
+    binding.attn_dense(q, k, v, out=dense, stream=side)
+    qb, kb, vs = binding.pool(q, k, v, 64, stream=side)
+    bits = torch.empty((2, 24, binding.sel_words(24)), dtype=torch.int32, device=q.device)
+    tau, kept2 = binding.route(qb, kb, 1500, 64, 1.0, sel_bits=bits, stream=side)
+    staged = binding.sweep(q, k, v, qb, kb, vs, tau, 64, sel_bits=bits, stream=side)
+    side.synchronize()
+    assert torch.equal(out, ref_out) and torch.equal(kept, ref_kept)
+    assert torch.equal(dense, ref_dense)
+    assert torch.equal(staged, ref_out) and torch.equal(kept2, ref_kept)
