@@ -154,9 +154,9 @@ __device__ __forceinline__ TileSrc tile_src(const u16* kp, const u16* vp, int ro
 template <int D, int BLK, int I = 0, int IEND = Sweep<D, BLK>::LPT>
 __device__ __forceinline__ void tile_issue(const TileSrc& src, u16* Kdst, u16* Vdst, int wave_s,
                                            uint32_t lane_base) {
-    using S = Sweep<D, BLK>;
     if constexpr (I < IEND) {
 #if defined(__HIP_DEVICE_COMPILE__)
+        using S = Sweep<D, BLK>;
         const int b = wave_s * S::LPT + I;
         const uint32_t off = lane_base + 2u * D * I;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(src.k, (lds_void_t*)(Kdst + S::kbase(b)), 16, off, 0, 0, 0);
