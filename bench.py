@@ -332,8 +332,14 @@ def main():
         "pool_gbs": pool_bytes / (st["pool"] * 1e-3) / 1e9,
         "dense_baseline": dense,
         "speedup_vs_dense": (dense["ms"] / head["ms"]) if dense else None,
+        # per beta: exact-tile flops over the whole forward's time (pool and
+        # route included) as a fraction of the bf16 peak, and the speedup
         "beta_sweep": [{"beta": r["beta"], "ms": r["ms"], "kept_frac": r["kept_frac"],
-                        "tflops_dense_eq": r["tflops_dense_eq"]} for r in results],
+                        "tflops_dense_eq": r["tflops_dense_eq"],
+                        "exact_tflop": r["F_exact"] / 1e12,
+                        "exact_util_of_forward": r["F_exact"] / (r["ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                        "speedup_vs_dense": (dense["ms"] / r["ms"]) if dense else None}
+                       for r in results],
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
