@@ -222,3 +222,14 @@ def test_side_stream_matches_default_stream():
     assert torch.equal(out, ref_out) and torch.equal(kept, ref_kept)
     assert torch.equal(dense, ref_dense)
     assert torch.equal(staged, ref_out) and torch.equal(kept2, ref_kept)
+
+
+@pytest.mark.parametrize("B,L", [(64, 200), (32, 200), (128, 700)])
+def test_many_heads_few_groups_per_head(B, L):
+    """50 heads with 2 (B = 64, 32) or 6 (B = 128) query groups each: some of
+    the eight per-XCD work queues are empty for every head, and (B = 64, 32)
+    the last group holds fewer query blocks than a full one; every element
+    against the oracle."""
+    inp = gen.random_inputs(50, L, 64, seed=15, dtype="bf16", scale=1.5)
+    s = run_and_check(inp, B, 0.5)
+    assert 0.0 < s["kept_frac"] < 1.0
