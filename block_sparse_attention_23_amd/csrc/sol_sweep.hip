@@ -12,9 +12,9 @@
 //      list follows: one approximate entry per chunk of max(B, 64) pooled
 //      keys that holds an unselected block of a query block, then one exact
 //      entry per key block that a query block selected (the union, so a key
-//      block chosen by several is loaded once; at B = 32, per aligned pair of
-//      key blocks 2j, 2j+1, one 64-key tile), each tagged with the query
-//      blocks that use it (at B = 32, per key block of the pair).
+//      block chosen by several is loaded once; at B = 32, one 64-key tile per
+//      two consecutive key blocks of the union), each tagged with the query
+//      blocks that use it (at B = 32 each wave reads its own block's bits).
 //   2. the tile loop over 64-key tiles.  Tiles stream from HBM straight into
 //      LDS (direct-to-LDS buffer loads, 16 bytes a lane) into two buffers, so
 //      the next tile loads while the current one is computed; the loads are
@@ -61,9 +61,10 @@ struct Sweep {
     static constexpr int SUB = TB / 64;                 // 64-key tiles per entry
     static constexpr int KPT = BLK < 64 ? 64 / BLK : 1;  // key blocks per exact 64-key tile (2 at B = 32)
     // tile-list entry: bit 31 approximate; bits PS .. 30 the query blocks
-    // that use it (exact entries at B = 32: bit h QB + b for key block 2j + h
-    // of the pair); bits 0 .. PS-1 the chunk, key block or pair index
-    static constexpr int PB = QB * KPT < 2 ? 2 : QB * KPT;
+    // that use it; bits 0 .. PS-1 the chunk or key block index.  Exact
+    // entries at B = 32 instead hold two key blocks: j1 in bits 0 .. 12, j2
+    // in bits 13 .. 25, bit 26 set when j2 is present.
+    static constexpr int PB = QB < 2 ? 2 : QB;
     static constexpr int PS = 31 - PB;
     static constexpr int CH = D / 8;                    // 16-byte chunks per row
     static constexpr int RPK = 1024 / (2 * D);          // rows per 1 KB of LDS
@@ -142,6 +143,20 @@ __device__ __forceinline__ TileSrc tile_src(const u16* kp, const u16* vp, int ro
     const int nbytes = __builtin_amdgcn_readfirstlane(max(0, min(64, rows - row0)) * D * 2);
     return TileSrc{__builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kp + (size_t)row0 * D), 0, nbytes, kRawBuffer),
                    __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vp + (size_t)row0 * D), 0, nbytes, kRawBuffer)};
+#else
+    return TileSrc{};
+#endif
+}
+
+// Buffer resources over rows 0 .. rows-1 of a source (B = 32 pairs: each
+// lane adds its own row offset).
+template <int D>
+__device__ __forceinline__ TileSrc rows_src(const u16* kp, const u16* vp, int rows) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int kRawBuffer = 0x00020000;
+    const int nbytes = __builtin_amdgcn_readfirstlane(rows * D * 2);
+    return TileSrc{__builtin_amdgcn_make_buffer_rsrc(uniform_ptr(kp), 0, nbytes, kRawBuffer),
+                   __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(vp), 0, nbytes, kRawBuffer)};
 #else
     return TileSrc{};
 #endif
@@ -289,21 +304,35 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                     if (part) tiles[nt + __popcll(m & ((1ull << lane) - 1ull))] = kApprox | (part << S::PS) | c;
                     nt += __popcll(m);
                 }
-                // exact key blocks (pairs of key blocks at B = 32), ascending
-                const int NE = (N + S::KPT - 1) / S::KPT;
-                for (int j0 = 0; j0 < NE; j0 += 64) {
-                    const int je = j0 + lane;
-                    uint32_t part = 0;
-#pragma unroll
-                    for (int hk = 0; hk < S::KPT; ++hk) {
-                        const int j = je * S::KPT + hk;
-                        if (je < NE && j < N)
+                // exact key blocks, ascending
+                if constexpr (S::KPT == 1) {
+                    for (int j0 = 0; j0 < N; j0 += 64) {
+                        const int j = j0 + lane;
+                        uint32_t part = 0;
+                        if (j < N)
                             for (int b = 0; b < nqb; ++b)
-                                part |= ((selbits[b * nwords + (j >> 5)] >> (j & 31)) & 1u) << (hk * S::QB + b);
+                                part |= ((selbits[b * nwords + (j >> 5)] >> (j & 31)) & 1u) << b;
+                        const uint64_t m = __ballot(part != 0);
+                        if (part) tiles[nt + __popcll(m & ((1ull << lane) - 1ull))] = (part << S::PS) | j;
+                        nt += __popcll(m);
                     }
-                    const uint64_t m = __ballot(part != 0);
-                    if (part) tiles[nt + __popcll(m & ((1ull << lane) - 1ull))] = (part << S::PS) | je;
-                    nt += __popcll(m);
+                } else {
+                    // B = 32: union element r goes to entry r / 2, as j1 (r
+                    // even) or j2 (r odd); within the one wave the j1 store
+                    // precedes the j2 read-modify-write of the same entry
+                    int nu = 0;
+                    for (int j0 = 0; j0 < N; j0 += 64) {
+                        const int j = j0 + lane;
+                        bool any = false;
+                        if (j < N)
+                            for (int b = 0; b < nqb; ++b) any |= ((selbits[b * nwords + (j >> 5)] >> (j & 31)) & 1u) != 0;
+                        const uint64_t m = __ballot(any);
+                        const int r = nu + __popcll(m & ((1ull << lane) - 1ull));
+                        if (any && !(r & 1)) tiles[nt + (r >> 1)] = (uint32_t)j;
+                        if (any && (r & 1)) tiles[nt + (r >> 1)] |= ((uint32_t)j << 13) | (1u << 26);
+                        nu += __popcll(m);
+                    }
+                    nt += (nu + 1) >> 1;
                 }
                 if (lane == 0) misc_s[1] = nt;
             }
@@ -350,11 +379,31 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             part = (d >> S::PS) & ((1u << S::PB) - 1u);
             row0 = (int)(d & ((1u << S::PS) - 1u)) * S::TB + (t % S::SUB) * 64;
         };
-        auto source_of = [&](uint32_t d, int t) {
+        // (B = 32 exact entries) the pair's key blocks
+        auto pair_of = [&](uint32_t d, int& j1, int& j2, bool& has2) {
+            j1 = (int)(d & 0x1FFFu);
+            j2 = (int)((d >> 13) & 0x1FFFu);
+            has2 = ((d >> 26) & 1u) != 0;
+        };
+        // lanes 0-31 load keys 0-31 of a tile and lanes 32-63 keys 32-63
+        const bool lo_lanes = lane < 32;
+        // resources of tile t and this lane's extra source offset (bytes)
+        auto source_of = [&](uint32_t d, int t, uint32_t& extra) {
             bool ap;
             uint32_t pt;
             int row0;
             decode(d, t, ap, pt, row0);
+            extra = 0;
+            if (S::KPT == 2 && !ap) {
+                // a pair: rows 32 j1 + k (k < 32) and 32 j2 + k - 32; an
+                // absent j2 points past L, so its loads are dropped
+                int j1, j2;
+                bool has2;
+                pair_of(d, j1, j2, has2);
+                const int rb = lo_lanes ? 32 * j1 : (has2 ? 32 * j2 - 32 : L);
+                extra = (uint32_t)rb * (2u * D);
+                return rows_src<D>(kg + head_off, vg + head_off, L);
+            }
             // choose the source before forming its resources (kept scalar)
             const u16* kp = ap ? a.kbar_bf + (size_t)h * N * D : kg + head_off;
             const u16* vp = ap ? a.vsum_bf + (size_t)h * N * D : vg + head_off;
@@ -373,14 +422,32 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             uint32_t part;
             int row0;
             decode(w_t, t, approx, part, row0);
-            // this wave's query block uses tile t (at B = 32: one of its key blocks)
-            const bool mine = ((part >> myb) | (S::KPT == 2 && !approx ? part >> (S::QB + myb) : 0u)) & 1u;
+            // B = 32 pairs: bit h of halves: this wave's query block selected
+            // key block h of the pair; lim_h: keys of half h before L
+            uint32_t halves = 3u;
+            int lim_h[2] = {0, 0};
+            if (S::KPT == 2 && !approx) {
+                int j1, j2;
+                bool has2;
+                pair_of(w_t, j1, j2, has2);
+                const uint32_t* sb = selbits + myb * nwords;
+                halves = ((sb[j1 >> 5] >> (j1 & 31)) & 1u) | (has2 ? ((sb[j2 >> 5] >> (j2 & 31)) & 1u) << 1 : 0u);
+                lim_h[0] = L - 32 * j1;
+                lim_h[1] = L - 32 * j2 + 32;
+            }
+            // this wave's query block uses tile t
+            const bool mine = S::KPT == 2 && !approx ? halves != 0u : ((part >> myb) & 1u) != 0u;
             if (t + 1 < TS) {  // tile t+1 streams into (Kn, Vn)
-                if (S::QB != 2 || part == 3u)
-                    tile_issue<D, BLK>(source_of(w_t1, t + 1), Kn, Vn, wave_s, dma_base);
-                else if (!mine)
-                    tile_issue<D, BLK, 0, 2 * S::LPT>(source_of(w_t1, t + 1), Kn, Vn, 2 * (wave_s & 1),
+                uint32_t extra;
+                if constexpr (S::KPT == 2) {
+                    const TileSrc nsrc = source_of(w_t1, t + 1, extra);
+                    tile_issue<D, BLK>(nsrc, Kn, Vn, wave_s, dma_base + extra);
+                } else if (S::QB != 2 || part == 3u) {
+                    tile_issue<D, BLK>(source_of(w_t1, t + 1, extra), Kn, Vn, wave_s, dma_base);
+                } else if (!mine) {
+                    tile_issue<D, BLK, 0, 2 * S::LPT>(source_of(w_t1, t + 1, extra), Kn, Vn, 2 * (wave_s & 1),
                                                       dma_base2);
+                }
             }
             const uint32_t raw2 = t + 2 < TS ? word_raw(t + 2) : 0u;
             // move the carried state on to tile t+1
@@ -420,9 +487,8 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             // this wave's query block did not select (exact).  Lane key
             // jj = 16 kt + 4g + r is bit 16 kt + r of colsel >> 4g.
             const int limit = approx ? N : L;
-            // bit h: this wave's query block uses key block h of the pair
-            const uint32_t halves = S::KPT == 2 && !approx ? ((part >> myb) & 1u) | (((part >> (S::QB + myb)) & 1u) << 1) : 3u;
-            if (approx || row0 + 64 > limit || halves != 3u) {
+            const bool pair = S::KPT == 2 && !approx;
+            if (approx || (pair ? (halves != 3u || lim_h[0] < 32 || lim_h[1] < 64) : row0 + 64 > limit)) {
                 uint64_t colsel = 0;
                 if (approx) {
                     const uint32_t* sb = selbits + myb * nwords;
@@ -438,7 +504,8 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                     for (int r = 0; r < 4; ++r) {
                         const int bit = kt * 16 + r;
                         const uint32_t w = bit < 32 ? cs_lo : cs_hi;
-                        const bool valid = g4 < lim - bit && !((w >> (bit & 31)) & 1u) && ((halves >> (kt >> 1)) & 1u);
+                        const bool valid = g4 < (pair ? lim_h[kt >> 1] : lim) - bit && !((w >> (bit & 31)) & 1u) &&
+                                           ((halves >> (kt >> 1)) & 1u);
                         if (!valid) sacc[kt][0][r] = sacc[kt][1][r] = -INFINITY;
                     }
             }
@@ -559,7 +626,13 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
         const int TS = T * S::SUB;
         if (TS > 0) {
             w_t = word_of(0, word_raw(0));
-            tile_issue<D, BLK>(source_of(w_t, 0), K0, V0, wave_s, dma_base);
+            uint32_t extra;
+            if constexpr (S::KPT == 2) {
+                const TileSrc src0 = source_of(w_t, 0, extra);
+                tile_issue<D, BLK>(src0, K0, V0, wave_s, dma_base + extra);
+            } else {
+                tile_issue<D, BLK>(source_of(w_t, 0, extra), K0, V0, wave_s, dma_base);
+            }
         }
         if (TS > 1) w_t1 = word_of(1, word_raw(1));
         for (int t = 0; t < TS; t += 2) {
