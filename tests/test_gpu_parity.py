@@ -233,3 +233,28 @@ def test_many_heads_few_groups_per_head(B, L):
     inp = gen.random_inputs(50, L, 64, seed=15, dtype="bf16", scale=1.5)
     s = run_and_check(inp, B, 0.5)
     assert 0.0 < s["kept_frac"] < 1.0
+
+
+def test_concurrent_calls_with_distinct_workspaces():
+    """Two forward passes in flight at once on two streams, each with its own
+    workspace, give the same bits as the same calls run one after another."""
+    a_in = grid_inp(2, 3000, 128, "bf16", seed=16)
+    b_in = grid_inp(3, 2100, 64, "bf16", seed=17)
+    qa, ka, va = to_device(a_in)
+    qb, kb, vb = to_device(b_in)
+    ref_a = binding.attn_fwd(qa, ka, va, 64, 1.0)
+    ref_b = binding.attn_fwd(qb, kb, vb, 128, 0.5)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    wa = binding.alloc_workspace(2, 3000, 128, 64, qa.device)
+    wb = binding.alloc_workspace(3, 2100, 64, 128, qb.device)
+    oa, ob = torch.empty_like(qa), torch.empty_like(qb)
+    kpa, kpb = torch.empty_like(ref_a[1]), torch.empty_like(ref_b[1])
+    torch.cuda.synchronize()
+    for _ in range(3):
+        binding.attn_fwd(qa, ka, va, 64, 1.0, out=oa, kept=kpa, workspace=wa, stream=s1)
+        binding.attn_fwd(qb, kb, vb, 128, 0.5, out=ob, kept=kpb, workspace=wb, stream=s2)
+    s1.synchronize()
+    s2.synchronize()
+    assert torch.equal(oa, ref_a[0]) and torch.equal(kpa, ref_a[1])
+    assert torch.equal(ob, ref_b[0]) and torch.equal(kpb, ref_b[1])
