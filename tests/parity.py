@@ -1,7 +1,7 @@
-"""Parity helpers: run the HIP path through the C ABI and judge it against the
+"""Parity helpers: run the HIP path through the C ABI and check it against the
 fp64 oracle on the same seeded inputs.
 
-Judging rule (spec tolerances, readings of the pages recorded with the
+Rule (the path's stated tolerances; readings of the pages recorded with the
 oracle):
   * selection: the kernel's exact/approximate decision per (h, i, j) equals
     the oracle's, except where |s_ij - tau_i| < 1e-3 in the oracle's values
@@ -64,7 +64,7 @@ def check_selection(q, k, v, B, beta, gsel, gkept, heads=None):
     return flips, okept / (H * N * N), (qbar, kbar, vsum)
 
 
-def judge_output(got, ref, dtype):
+def check_output(got, ref, dtype):
     tmax, tmean = TOL[dtype]
     err = np.abs(got.astype(np.float64) - ref)
     stats = {"max_err": float(err.max()), "mean_err": float(err.mean())}
@@ -103,6 +103,6 @@ def run_and_check(inp, B, beta, rows=None, sel_heads=None):
         hidx = torch.tensor([hs[h] for h in rows[:, 0]], device=out.device, dtype=torch.long)
         ridx = torch.tensor(rows[:, 1], device=out.device, dtype=torch.long)
         got = out[hidx, ridx].float().cpu().numpy()
-    stats = judge_output(got, ref, w.dtype)
+    stats = check_output(got, ref, w.dtype)
     stats.update(flips=flips, kept_frac=float(gsel.mean()), oracle_kept_frac=okept)
     return stats

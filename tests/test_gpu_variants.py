@@ -17,7 +17,7 @@ import oracle
 from block_sparse_attention_23_amd import binding
 from block_sparse_attention_23_amd import inputs as gen
 
-from .parity import FLIP_BAND, TOL, block_rows, check_selection, judge_output, to_device
+from .parity import FLIP_BAND, TOL, block_rows, check_selection, check_output, to_device
 
 pytestmark = pytest.mark.gpu
 INF = math.inf
@@ -62,7 +62,7 @@ def run_variant(inp, B, beta, keep_frac, drop, topk, rows=None):
     else:
         got = out[torch.tensor(rows[:, 0], device=out.device, dtype=torch.long),
                   torch.tensor(rows[:, 1], device=out.device, dtype=torch.long)].float().cpu().numpy()
-    stats = judge_output(got, ref, "bf16")
+    stats = check_output(got, ref, "bf16")
     stats["kept_frac"] = float(gsel.mean())
     return stats, out
 
