@@ -1,7 +1,7 @@
 """Build the fp64 CPU oracle (``liboracle.so``) with gcc + OpenMP.
 
-Test infrastructure: the oracle is the checker for the HIP library and is
-built beside it, never linked into it.
+Test infrastructure: the oracle is the reference the HIP library is tested
+against; it is built beside it, never linked into it.
 """
 import os
 import subprocess

@@ -1,7 +1,8 @@
 /*
  * sol_oracle.c -- plain fp64 CPU oracle of the Sol-Attn forward pass.
  *
- * TEST INFRASTRUCTURE ONLY.  This file is the checker, not the product: only
+ * TEST INFRASTRUCTURE ONLY.  This file is the reference the HIP library is
+ * tested against, not the product: only
  * the test suite, the smoke check and the benchmark's CPU-baseline leg may load
  * it.  It shares no code, header, table or helper with the HIP library.
  *
