@@ -288,6 +288,15 @@ def main():
         st["sweep"] += e[2].elapsed_time(e[3]) / args.steps
     log(f"[bench] stages at beta={beta0}: " + ", ".join(f"{k} {v:.3f} ms" for k, v in st.items()))
     F_alg = head["F_exact"] + head["F_approx"]
+    # token-pair density at the headline beta: selected (i, j) pairs weighted
+    # by the valid tokens n_i n_j (only the last block is short)
+    nlast = L - (N - 1) * B
+    kept_h = kept.to(torch.float64)  # the staged route wrote the headline beta's counts
+    last_sel = ((bits[:, :, (N - 1) // 32] >> ((N - 1) % 32)) & 1).to(torch.float64)
+    n_i = torch.full((N,), float(B), dtype=torch.float64, device="cuda")
+    n_i[N - 1] = nlast
+    pair_tokens = (n_i[None, :] * (kept_h * B - (B - nlast) * last_sel)).sum().item()
+    kept_token_pair_frac = pair_tokens / (H * float(L) * L)
     achieved = F_alg / (st["sweep"] * 1e-3) / 1e12
     pool_bytes = 3.0 * H * L * d * (2 if w.dtype == "bf16" else 4) + 3.0 * H * N * d * 4
     traffic = measured_traffic()
@@ -322,6 +331,7 @@ def main():
         "config": {"workload": f"{w.name}: {w.desc}", "H": H, "L": L, "d": d, "B": B,
                    "N": N, "beta": head["beta"], "seed": w.seed},
         "kept_block_frac": head["kept_frac"],
+        "kept_token_pair_frac": kept_token_pair_frac,
         "exact_tile_mfma_util": head["F_exact"] / (st["sweep"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
