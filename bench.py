@@ -107,6 +107,17 @@ def time_loop(fn, steps, warmup, torch):
     return e0.elapsed_time(e1) / steps, wall
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None where absent)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, inp, beta, target_s):
     """The fp64 oracle on a bounded sample of about target_s seconds: heads
     0, 1, ... in turn, each with pool + route of the whole head and then the
@@ -145,7 +156,7 @@ def cpu_baseline(w, inp, beta, target_s):
         desc += ("; " if desc else "") + f"head {h}: first {n} query blocks ({rows_n} rows)"
     return {
         "value": flops / total / 1e12, "unit": "dense-equiv TFLOP/s", "cores": oracle.num_threads(),
-        "kind": "oracle",
+        "kind": "oracle", "cpu_model": cpu_model(),
         "sample": (f"{w.name} at beta={beta}: per head, pool + route of the whole head and the "
                    f"merge of its query blocks; {desc} = {flops / 1e12:.3f} dense-equiv TFLOP "
                    f"in {total:.1f} s"),
