@@ -287,7 +287,7 @@ def main():
         if e: e[0].record(s)
         binding.pool(q, k, v, B, outs=(qbar, kbar, vsum))
         if e: e[1].record(s)
-        binding.route(qbar, kbar, L, B, beta0, tau=tau, kept=kept, sel_bits=bits)
+        binding.route(qbar, kbar, L, B, beta0, tau=tau, kept=kept, sel_bits=bits, workspace=ws)
         if e: e[2].record(s)
         binding.sweep(q, k, v, qbar, kbar, vsum, tau, B, out=out, workspace=ws, sel_bits=bits)
         if e: e[3].record(s)

@@ -20,7 +20,7 @@ _FUNCS = {
     "sol_pool": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 5
                  + [ctypes.c_void_p] * 4),
     "sol_route": (ctypes.c_int, [ctypes.c_void_p] * 2 + [ctypes.c_int] * 4
-                  + [ctypes.c_float] + [ctypes.c_void_p] * 4),
+                  + [ctypes.c_float] + [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]),
     "sol_sweep": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 5
                   + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t] + [ctypes.c_void_p] * 3),
     "sol_attn_fwd": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4
@@ -131,7 +131,7 @@ def pool(q, k, v, B, outs=None, stream=None):
     return tuple(outs)
 
 
-def route(qbar, kbar, L, B, beta, tau=None, kept=None, sel_bits=None, stream=None):
+def route(qbar, kbar, L, B, beta, tau=None, kept=None, sel_bits=None, workspace=None, stream=None):
     """Thresholds tau [H][N] and kept counts [H][N] from pooled tensors; with
     sel_bits (int32 [H][N][ceil(N/32)]) also the decisions as bits."""
     H, N, d = qbar.shape
@@ -141,10 +141,13 @@ def route(qbar, kbar, L, B, beta, tau=None, kept=None, sel_bits=None, stream=Non
         tau = torch.empty((H, N), dtype=torch.float32, device=qbar.device)
     if kept is None:
         kept = torch.empty((H, N), dtype=torch.int32, device=qbar.device)
+    if workspace is None:
+        workspace = alloc_workspace(H, L, d, B, qbar.device)
     with torch.cuda.device(qbar.device):
         _check("sol_route", lib().sol_route(qbar.data_ptr(), kbar.data_ptr(), H, L, d, B,
                                             float(beta), tau.data_ptr(), kept.data_ptr(),
                                             None if sel_bits is None else sel_bits.data_ptr(),
+                                            workspace.data_ptr(), workspace.numel(),
                                             _stream_ptr(stream, qbar.device)))
     return tau, kept
 

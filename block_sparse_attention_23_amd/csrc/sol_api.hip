@@ -42,6 +42,7 @@ int check_tensors(const void* q, const void* k, const void* v, const void* out, 
 //   queues           : int32[8]           sweep work counters
 //   kbar_bf, vsum_bf : bf16 [H][N][d]     MFMA operands of the approximate path
 //   sel              : u32  [H][N][W]     selection bits, W = ceil(N / 32)
+//   mom              : fp32 [H][d + d*d]  key moments (routing rows longer than LDS holds)
 struct Workspace {
     float* qbar;
     float* kbar;
@@ -51,6 +52,7 @@ struct Workspace {
     uint16_t* kbar_bf;
     uint16_t* vsum_bf;
     uint32_t* sel;
+    float* mom;
     size_t bytes;
 };
 
@@ -61,6 +63,7 @@ Workspace carve(void* base, int H, int L, int d, int B) {
     const size_t taub = align_up(sizeof(float) * (size_t)H * N);
     const size_t qb = align_up(sizeof(int) * 8);
     const size_t selb = align_up(sizeof(uint32_t) * (size_t)H * N * ((N + 31) / 32));
+    const size_t momb = align_up(sizeof(float) * (size_t)H * ((size_t)d + (size_t)d * d));
     char* p = static_cast<char*>(base);
     Workspace w;
     size_t off = 0;
@@ -72,6 +75,7 @@ Workspace carve(void* base, int H, int L, int d, int B) {
     w.kbar_bf = reinterpret_cast<uint16_t*>(p + off); off += pooled_bf;
     w.vsum_bf = reinterpret_cast<uint16_t*>(p + off); off += pooled_bf;
     w.sel = reinterpret_cast<uint32_t*>(p + off); off += selb;
+    w.mom = reinterpret_cast<float*>(p + off); off += momb;
     w.bytes = off;
     return w;
 }
@@ -132,7 +136,7 @@ int forward(const void* q, const void* k, const void* v, int H, int L, int d, in
                          ? static_cast<int>(fmin((double)N, fmax(0.0, floor((double)keep_frac * N + 0.5))))
                          : -1;
     if (sol::launch_route(w.qbar, w.kbar, H, N, d, c, beta, nullptr, tau, kept, sel, w.queues, s,
-                          topk) != hipSuccess)
+                          topk, w.mom) != hipSuccess)
         return SOL_EHIP;
     sol::AttnArgs a = sweep_args(q, k, v, w.qbar, w.kbar, w.vsum, tau, w.kbar_bf, w.vsum_bf, H, L,
                                  d, B, out, w.queues, sel);
@@ -166,17 +170,21 @@ int sol_pool(const void* q, const void* k, const void* v, int H, int L, int d, i
 }
 
 int sol_route(const float* qbar, const float* kbar, int H, int L, int d, int B, float beta,
-              float* tau, int32_t* kept_counts, uint32_t* sel_bits, void* stream) {
+              float* tau, int32_t* kept_counts, uint32_t* sel_bits, void* workspace,
+              size_t ws_bytes, void* stream) {
     int st = check_shape(H, L, d, B);
     if (st != SOL_OK) return st;
     if (!qbar || !kbar || !tau || !kept_counts || isnan(beta)) return SOL_EINVAL;
     if (!aligned(qbar, 16) || !aligned(kbar, 16) || !aligned(tau, 4) || !aligned(kept_counts, 4) ||
         (sel_bits && !aligned(sel_bits, 4)))
         return SOL_EINVAL;
+    if (!workspace || !aligned(workspace, kAlign)) return SOL_EWORKSPACE;
+    const Workspace w = carve(workspace, H, L, d, B);
+    if (ws_bytes < w.bytes) return SOL_EWORKSPACE;
     const int N = (L + B - 1) / B;
     const float c = static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
     if (sol::launch_route(qbar, kbar, H, N, d, c, beta, nullptr, tau, kept_counts, sel_bits, nullptr,
-                          static_cast<hipStream_t>(stream)) != hipSuccess)
+                          static_cast<hipStream_t>(stream), -1, w.mom) != hipSuccess)
         return SOL_EHIP;
     return SOL_OK;
 }

@@ -37,9 +37,11 @@ hipError_t launch_pooled_to_bf16(const float* kbar, const float* vsum, size_t n,
 // topk >= 0: the fixed-budget comparator instead of the threshold rule
 // (the k = topk largest scores of every row, ties to the lower index;
 // tau = the k-th largest score); beta and tau_in are then unused.
+// mom: H (d + d*d) floats of scratch for the key moments, needed when
+// threshold rows are too long for LDS (N > 1280) and tau is computed.
 hipError_t launch_route(const float* qbar, const float* kbar, int H, int N, int d, float c,
                         float beta, const float* tau_in, float* tau, int32_t* kept, uint32_t* sel,
-                        int* queues, hipStream_t s, int topk = -1);
+                        int* queues, hipStream_t s, int topk = -1, float* mom = nullptr);
 hipError_t launch_sweep_bf16(const AttnArgs& a, int d, int B, bool dense, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int d, int B, bool dense, hipStream_t s);
 hipError_t launch_reset_counters(int* queues, hipStream_t s);

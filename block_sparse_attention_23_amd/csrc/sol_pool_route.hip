@@ -325,6 +325,193 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
 }
 
 // ============================================================================
+// key moments (Eq. (5)): per head the mean of the pooled keys
+// mbar = (1/N) sum_j kbar_j and their second moments
+// C = (1/N) sum_j kbar_j kbar_j^T, from which the proxy row's population
+// mean and variance follow without forming the row:
+// mu_i = c qbar_i . mbar and sigma_i^2 = c^2 qbar_i C qbar_i^T - mu_i^2.
+// Workgroup (h, bi, bj) forms the 32x32 block (bi, bj) of C (and, for
+// bj = 0, 32 entries of mbar), summing over j in a fixed order.  Per head:
+// mbar, then C row-major (D + D*D floats).
+// ============================================================================
+template <int D>
+__global__ void __launch_bounds__(256) key_moments_kernel(const float* __restrict__ kbar, int N,
+                                                          float* __restrict__ mom) {
+    constexpr int NBK = D / 32;
+    __shared__ float ka[64][33];
+    __shared__ float kb[64][33];
+    const int h = blockIdx.x / (NBK * NBK);
+    const int bi = (blockIdx.x / NBK) % NBK, bj = blockIdx.x % NBK;
+    const int tid = threadIdx.x, a = tid >> 3, b4 = (tid & 7) * 4;
+    const float* kh = kbar + (size_t)h * N * D;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float macc = 0.0f;
+    for (int j0 = 0; j0 < N; j0 += 64) {
+        __syncthreads();
+        for (int x = tid; x < 64 * 32; x += 256) {
+            const int jj = x >> 5, e = x & 31, j = j0 + jj;
+            ka[jj][e] = j < N ? kh[(size_t)j * D + 32 * bi + e] : 0.0f;
+            kb[jj][e] = j < N ? kh[(size_t)j * D + 32 * bj + e] : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll 8
+        for (int jj = 0; jj < 64; ++jj) {
+            const float x = ka[jj][a];
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) acc[cc] = __builtin_fmaf(x, kb[jj][b4 + cc], acc[cc]);
+            macc += x;
+        }
+    }
+    const float inv = 1.0f / static_cast<float>(N);
+    float* mh = mom + (size_t)h * (D + D * D);
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) mh[D + (32 * bi + a) * D + 32 * bj + b4 + cc] = acc[cc] * inv;
+    if (bj == 0 && b4 == 0) mh[32 * bi + a] = macc * inv;
+}
+
+// ============================================================================
+// route from the key moments, for rows too long to hold in LDS (N > 1280):
+// per (h, i) the threshold tau_i = mu_i + beta sigma_i (Eq. (4)) with mu_i
+// and sigma_i from the moments (Eq. (5), above), then one pass that forms
+// every s_ij (Eq. (11) right-hand side) exactly as the row-holding route
+// does and keeps only the decision s_ij > tau_i, as bits, and their count.
+// One workgroup serves 16 query blocks (one MFMA row tile).  With tau_in,
+// or beta = +-inf, the thresholds need no moments.
+// ============================================================================
+template <int D>
+__global__ void __launch_bounds__(256) route_moments_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kbar, const float* __restrict__ mom,
+    int N, int groups_per_head, float c, float beta, const float* __restrict__ tau_in,
+    float* __restrict__ tau_out, int32_t* __restrict__ kept, uint32_t* __restrict__ sel, int W,
+    int* __restrict__ queues) {
+    constexpr int R = 16;
+    extern __shared__ uint16_t bits16[];  // [R][NKT]: the decisions on 16-key tile kt of row r
+    __shared__ float qs[R][D + 1];
+    __shared__ float tau_s[R];
+    const int h = blockIdx.x / groups_per_head;
+    const int i0 = (blockIdx.x % groups_per_head) * R;
+    const int nr = min(R, N - i0);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int NKT = (N + 15) / 16;
+    if (queues && blockIdx.x == 0 && tid < 8) queues[tid] = 0;
+    for (int x = tid; x < R * D; x += 256) {
+        const int r = x / D, e = x % D;
+        qs[r][e] = qbar[((size_t)h * N + min(i0 + r, N - 1)) * D + e];
+    }
+    __syncthreads();
+
+    // thresholds: wave w takes rows 4w .. 4w+3, lane l the columns l + 64 m of
+    // v = qbar_r C, then e_r = v . qbar_r and qbar_r . mbar by butterflies
+    if (tau_in || isinf(beta)) {
+        if (tid < R) tau_s[tid] = tau_in ? tau_in[(size_t)h * N + min(i0 + tid, N - 1)] : beta;
+    } else {
+        constexpr int CPL = D / 64;
+        const float* mh = mom + (size_t)h * (D + D * D);
+        float v[4][CPL];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+            for (int m = 0; m < CPL; ++m) v[rr][m] = 0.0f;
+#pragma unroll 4
+        for (int dp = 0; dp < D; ++dp) {
+            float crow[CPL];
+#pragma unroll
+            for (int m = 0; m < CPL; ++m) crow[m] = mh[D + dp * D + lane + 64 * m];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const float qd = qs[4 * wave + rr][dp];
+#pragma unroll
+                for (int m = 0; m < CPL; ++m) v[rr][m] = __builtin_fmaf(qd, crow[m], v[rr][m]);
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const int r = 4 * wave + rr;
+            float e = 0.0f, mu = 0.0f;
+#pragma unroll
+            for (int m = 0; m < CPL; ++m) {
+                const int col = lane + 64 * m;
+                e = __builtin_fmaf(qs[r][col], v[rr][m], e);
+                mu = __builtin_fmaf(qs[r][col], mh[col], mu);
+            }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                e += __shfl_xor(e, off);
+                mu += __shfl_xor(mu, off);
+            }
+            if (lane == 0) {
+                const float m_ = c * mu;
+                const float var = fmaxf(c * c * e - m_ * m_, 0.0f);
+                tau_s[r] = __builtin_fmaf(beta, sqrtf(var), m_);
+            }
+        }
+    }
+    __syncthreads();
+
+    // decisions: the proxy scores as the row-holding route forms them (fp32
+    // MFMA, the same operands and order), compared as they leave the MFMA
+    const int l16 = lane & 15, g = lane >> 4;
+    constexpr int QD = D / 4;
+    float qv[QD];
+#pragma unroll
+    for (int e = 0; e < QD; ++e) qv[e] = qs[l16][g * QD + e];
+    const float* kh = kbar + (size_t)h * N * D;
+    float tr[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) tr[x] = tau_s[4 * g + x];
+    auto kload = [&](int kt, float (&kv)[QD]) __attribute__((always_inline)) {
+        const float4* src = reinterpret_cast<const float4*>(kh + (size_t)min(kt * 16 + l16, N - 1) * D + g * QD);
+#pragma unroll
+        for (int e = 0; e < QD / 4; ++e) {
+            const float4 t = src[e];
+            kv[4 * e] = t.x; kv[4 * e + 1] = t.y; kv[4 * e + 2] = t.z; kv[4 * e + 3] = t.w;
+        }
+    };
+    auto decide = [&](int kt, const float (&kv)[QD]) __attribute__((always_inline)) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < QD; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[st], kv[st], acc, 0, 0, 0);
+        const int j = kt * 16 + l16;  // lane holds rows 4g .. 4g+3 of key j
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const uint64_t m = __ballot(j < N && acc[x] * c > tr[x]);
+            // lanes 16 g' .. 16 g' + 15 hold row 4 g' + x
+            if (l16 == 0) bits16[(4 * g + x) * NKT + kt] = static_cast<uint16_t>(m >> (16 * g));
+        }
+    };
+    float kva[QD], kvb[QD];
+    if (wave < NKT) kload(wave, kva);
+#pragma unroll 1
+    for (int kt = wave; kt < NKT; kt += 8) {
+        if (kt + 4 < NKT) kload(kt + 4, kvb);
+        decide(kt, kva);
+        if (kt + 4 >= NKT) break;
+        if (kt + 8 < NKT) kload(kt + 8, kva);
+        decide(kt + 4, kvb);
+    }
+    __syncthreads();
+
+    // bits out (bit j % 32 of word j / 32) and the counts
+    if (sel)
+        for (int x = tid; x < nr * W; x += 256) {
+            const int r = x / W, w = x % W;
+            const uint32_t lo = bits16[r * NKT + 2 * w];
+            const uint32_t hi = 2 * w + 1 < NKT ? bits16[r * NKT + 2 * w + 1] : 0u;
+            sel[((size_t)h * N + i0 + r) * W + w] = lo | (hi << 16);
+        }
+    for (int r = wave; r < nr; r += 4) {
+        int cnt = 0;
+        for (int kt = lane; kt < NKT; kt += 64) cnt += __popc(bits16[r * NKT + kt]);
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
+        if (lane == 0 && !tau_in) {
+            tau_out[(size_t)h * N + i0 + r] = tau_s[r];
+            kept[(size_t)h * N + i0 + r] = cnt;
+        }
+    }
+}
+
+// ============================================================================
 // launchers
 // ============================================================================
 namespace {
@@ -356,13 +543,36 @@ hipError_t route_t(const float* qbar, const float* kbar, int H, int N, float c, 
 }
 
 template <int D>
-hipError_t route_d(const float* qbar, const float* kbar, int H, int N, float c, float beta,
+hipError_t route_moments_t(const float* qbar, const float* kbar, float* mom, int H, int N, float c,
+                           float beta, const float* tau_in, float* tau, int32_t* kept, uint32_t* sel,
+                           int* queues, hipStream_t s) {
+    if (!tau_in && !isinf(beta)) {
+        if (!mom) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((key_moments_kernel<D>), dim3(H * (D / 32) * (D / 32)), dim3(256), 0, s, kbar, N,
+                           mom);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int gph = (N + 15) / 16;
+    const size_t shm = sizeof(uint16_t) * 16 * (size_t)((N + 15) / 16);
+    hipLaunchKernelGGL((route_moments_kernel<D>), dim3(H * gph), dim3(256), shm, s, qbar, kbar,
+                       static_cast<const float*>(mom), N, gph, c, beta, tau_in, tau, kept, sel, (N + 31) / 32,
+                       queues);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t route_d(const float* qbar, const float* kbar, float* mom, int H, int N, float c, float beta,
                    const float* tau_in, float* tau, int32_t* kept, uint32_t* sel, int* queues,
                    int topk, hipStream_t s) {
     // as many rows per workgroup (at most one 16-row MFMA tile) as 80 KB of
-    // LDS holds (two workgroups per CU share its 160 KB)
+    // LDS holds (two workgroups per CU share its 160 KB); threshold routing
+    // with longer rows takes its statistics from the key moments instead
+    // and serves 16 rows per workgroup without holding them
     const size_t row_bytes = sizeof(float) * (size_t)N;
     constexpr size_t kLds = 80 * 1024;
+    if (topk < 0 && 16 * row_bytes > kLds)
+        return route_moments_t<D>(qbar, kbar, mom, H, N, c, beta, tau_in, tau, kept, sel, queues, s);
 #define SOL_ROUTE(R) route_t<D, R>(qbar, kbar, H, N, c, beta, tau_in, tau, kept, sel, queues, topk, s)
     if (16 * row_bytes <= kLds) return SOL_ROUTE(16);
     if (8 * row_bytes <= kLds) return SOL_ROUTE(8);
@@ -403,9 +613,9 @@ hipError_t launch_reset_counters(int* queues, hipStream_t s) {
 
 hipError_t launch_route(const float* qbar, const float* kbar, int H, int N, int d, float c,
                         float beta, const float* tau_in, float* tau, int32_t* kept, uint32_t* sel,
-                        int* queues, hipStream_t s, int topk) {
-    if (d == 64) return route_d<64>(qbar, kbar, H, N, c, beta, tau_in, tau, kept, sel, queues, topk, s);
-    if (d == 128) return route_d<128>(qbar, kbar, H, N, c, beta, tau_in, tau, kept, sel, queues, topk, s);
+                        int* queues, hipStream_t s, int topk, float* mom) {
+    if (d == 64) return route_d<64>(qbar, kbar, mom, H, N, c, beta, tau_in, tau, kept, sel, queues, topk, s);
+    if (d == 128) return route_d<128>(qbar, kbar, mom, H, N, c, beta, tau_in, tau, kept, sel, queues, topk, s);
     return hipErrorInvalidValue;
 }
 

@@ -47,10 +47,12 @@ typedef enum {
 } sol_status_t;
 
 /*
- * Bytes of device workspace sol_attn_fwd / sol_attn_fwd_dbg need for this
- * shape: the pooled tensors (3 x H*N*d fp32), the per-query-block thresholds
- * (H*N fp32), the scheduler's queue counters and bf16 copies of the pooled
- * keys and summed values (2 x H*N*d bf16).  0 for invalid shapes.
+ * Bytes of device workspace sol_attn_fwd / sol_attn_fwd_dbg (and sol_route,
+ * sol_sweep) need for this shape: the pooled tensors (3 x H*N*d fp32), the
+ * per-query-block thresholds (H*N fp32), the scheduler's queue counters, bf16
+ * copies of the pooled keys and summed values (2 x H*N*d bf16), the
+ * selection bits (H*N*ceil(N/32) uint32) and the key moments
+ * (H*(d + d*d) fp32).  0 for invalid shapes.
  */
 size_t sol_workspace_bytes(int H, int L, int d, int B);
 
@@ -80,13 +82,20 @@ int sol_pool(const void* q, const void* k, const void* v,
  *              decisions themselves, bit (j % 32) of word j / 32 of row (h, i)
  *              set iff s_ij > tau_i (the layout of sol_attn_fwd_dbg's
  *              sel_mask).  sol_sweep can take them instead of deriving them.
- * The counts and bits are those the forward pass uses (the same kernel
- * forms every s_ij, by fp32 matrix instructions; both sweeps take their
+ * workspace  : DEVICE, at least sol_workspace_bytes(H, L, d, B) bytes,
+ *              256-byte aligned (scratch; missing or small: SOL_EWORKSPACE).
+ * For N <= 1280 each row s_i. is held on chip and mu_i, sigma_i are its
+ * two-pass statistics.  For longer rows mu_i and sigma_i come from the key
+ * moments of Eq. (5), mu_i = c qbar_i . mbar and sigma_i^2 = c^2 qbar_i C
+ * qbar_i^T - mu_i^2 with mbar = (1/N) sum_j kbar_j and C = (1/N) sum_j
+ * kbar_j kbar_j^T (computed into the workspace), equal in exact arithmetic.
+ * The counts and bits are those the forward pass uses (the same kernels
+ * form every s_ij, by fp32 matrix instructions; both sweeps take their
  * decisions from these bits).
  */
 int sol_route(const float* qbar, const float* kbar, int H, int L, int d, int B,
               float beta, float* tau, int32_t* kept_counts, uint32_t* sel_bits,
-              void* stream);
+              void* workspace, size_t ws_bytes, void* stream);
 
 /*
  * The fused sweep alone: given the pooled tensors and thresholds, route each

@@ -97,10 +97,12 @@ def test_pool_and_dense_reject_bad_arguments(lib):
 
 
 def test_stage_entry_points_reject_bad_arguments(lib):
-    assert lib.sol_route(FAKE, None, 1, 100, 64, 64, 1.0, FAKE, FAKE, None, None) == -1
-    assert lib.sol_route(FAKE, FAKE, 1, 100, 64, 64, math.nan, FAKE, FAKE, None, None) == -1
-    assert lib.sol_route(FAKE, FAKE, 1, 100, 64, 16, 1.0, FAKE, FAKE, None, None) == -2
-    assert lib.sol_route(FAKE, FAKE, 1, 100, 64, 64, 1.0, FAKE, FAKE, FAKE + 2, None) == -1
+    assert lib.sol_route(FAKE, None, 1, 100, 64, 64, 1.0, FAKE, FAKE, None, FAKE_WS, 1 << 30, None) == -1
+    assert lib.sol_route(FAKE, FAKE, 1, 100, 64, 64, math.nan, FAKE, FAKE, None, FAKE_WS, 1 << 30, None) == -1
+    assert lib.sol_route(FAKE, FAKE, 1, 100, 64, 16, 1.0, FAKE, FAKE, None, FAKE_WS, 1 << 30, None) == -2
+    assert lib.sol_route(FAKE, FAKE, 1, 100, 64, 64, 1.0, FAKE, FAKE, FAKE + 2, FAKE_WS, 1 << 30, None) == -1
+    assert lib.sol_route(FAKE, FAKE, 1, 100, 64, 64, 1.0, FAKE, FAKE, None, None, 1 << 30, None) == -3
+    assert lib.sol_route(FAKE, FAKE, 1, 100, 64, 64, 1.0, FAKE, FAKE, None, FAKE_WS, 16, None) == -3
     args = [FAKE] * 7 + [1, 100, 64, 64, 0, FAKE, FAKE_WS, 1 << 30, None, None, None]
     bad = list(args)
     bad[13] = None  # workspace

@@ -156,7 +156,7 @@ def test_workspace_reuse_across_shapes():
 
 @pytest.mark.parametrize("dtype,d,B,L", [("bf16", 128, 64, 1000), ("bf16", 64, 128, 700),
                                          ("fp32", 64, 64, 500), ("bf16", 128, 32, 1000),
-                                         ("fp32", 128, 32, 300)])
+                                         ("fp32", 128, 32, 300), ("bf16", 64, 32, 45000)])
 def test_stage_entry_points_equal_forward(dtype, d, B, L):
     """sol_pool -> sol_route -> sol_sweep (with the route's selection bits, and
     without them) launches the forward pass's own kernels: identical output,
