@@ -460,7 +460,8 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
 
             // S^T = K Q^T for this wave's 32 query rows, one 32-deep step at a
             // time; the K fragments of step s+1 are read before the MFMAs of
-            // step s, so each batch of LDS reads hides behind MFMA work.
+            // step s, so each batch of LDS reads hides behind MFMA work (the
+            // compiler's MFMA / LDS interleaving strategy 1 orders them).
             f32x4_t sacc[4][2];
             u32x4_t kfr[2][4];
             auto kread = [&](int st, u32x4_t (&dst)[4]) __attribute__((always_inline)) {
@@ -471,15 +472,14 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             kread(0, kfr[0]);
 #pragma unroll
             for (int st = 0; st < S::NS; ++st) {
+                if (st == 0) __builtin_amdgcn_iglp_opt(1);
                 if (st + 1 < S::NS) kread(st + 1, kfr[(st + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int kt = 0; kt < 4; ++kt) {
                     const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
                     sacc[kt][0] = mfma16(as_bf16x8(kfr[st & 1][kt]), qf[0][st], st == 0 ? z : sacc[kt][0]);
                     sacc[kt][1] = mfma16(as_bf16x8(kfr[st & 1][kt]), qf[1][st], st == 0 ? z : sacc[kt][1]);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
 
             // column masks: tokens past L (exact), selected or past-N pooled
@@ -588,7 +588,8 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                                         pack_bf16x2(sacc[2 * u + 1][qt][2], sacc[2 * u + 1][qt][3])};
             // V^T operands in batches of VB d-tiles (batch b: 32-key step
             // u = b / NVB, d-tiles VB (b % NVB) ...); batch b+1 is read
-            // before the MFMAs of batch b.
+            // before the MFMAs of batch b (ordered, as above, by the
+            // compiler's interleaving strategy 1).
             constexpr int VB = S::NDT >= 4 ? 4 : S::NDT;
             constexpr int NVB = S::NDT / VB;
             bf16x8_t vfr[2][VB];
@@ -608,8 +609,8 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
 #pragma unroll
             for (int b = 0; b < 2 * NVB; ++b) {
                 const int u = b / NVB, d0 = (b % NVB) * VB;
+                if (b == 0) __builtin_amdgcn_iglp_opt(1);
                 if (b + 1 < 2 * NVB) vread(b + 1, vfr[(b + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int db = 0; db < VB; ++db) {
                     o[d0 + db][0] = mfma16(vfr[b & 1][db], as_bf16x8(pb[u][0]), o[d0 + db][0]);
@@ -619,7 +620,6 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                     o[S::NDT][0] = mfma16(as_bf16x8(wrow[u]), as_bf16x8(pb[u][0]), o[S::NDT][0]);
                     o[S::NDT][1] = mfma16(as_bf16x8(wrow[u]), as_bf16x8(pb[u][1]), o[S::NDT][1]);
                 }
-                __builtin_amdgcn_sched_barrier(0);
             }
         };
 
