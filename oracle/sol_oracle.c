@@ -143,12 +143,21 @@ int sol_oracle_route(const double* qbar, const double* kbar,
                     for (int x = 0; x < d; ++x) s += qi[x] * kj[x];
                     row[j] = c * s;
                 }
-                double m = 0.0;
-                for (int j = 0; j < N; ++j) m += row[j];
-                m /= (double)N;
-                double var = 0.0;
-                for (int j = 0; j < N; ++j) var += (row[j] - m) * (row[j] - m);
-                var /= (double)N;
+                /* a constant row's mean is its common value and its variance
+                   is 0 (Eq. (5) with every s_ij equal); a sum of N equal fp64
+                   terms divided by N need not give the value back, so such
+                   a row takes these exact statistics directly */
+                int flat = 1;
+                for (int j = 1; j < N; ++j) flat &= row[j] == row[0];
+                double m = 0.0, var = 0.0;
+                if (flat) {
+                    m = row[0];
+                } else {
+                    for (int j = 0; j < N; ++j) m += row[j];
+                    m /= (double)N;
+                    for (int j = 0; j < N; ++j) var += (row[j] - m) * (row[j] - m);
+                    var /= (double)N;
+                }
                 const double sg = sqrt(var > 0.0 ? var : 0.0);
                 double t;
                 if (isinf(beta)) t = beta; /* -inf: keep all, +inf: keep none */

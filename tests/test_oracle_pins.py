@@ -143,6 +143,18 @@ def test_threshold_is_strict_and_infinite_betas():
         assert np.all(r["sigma"] == 0.0)
     assert oracle.route(qbar, kbar, float("-inf"))["kept"].min() == N
     assert oracle.route(qbar, kbar, float("inf"))["kept"].max() == 0
+    # a constant row of non-dyadic scores (equal pooled keys, random query):
+    # the scores are bitwise equal, so mu is that score, sigma = 0 and no
+    # block is strictly above tau, although a sum of 37 equal fp64 terms
+    # over 37 need not return the score
+    qr = rng.standard_normal((2, 37, 16))
+    kr = np.tile(rng.standard_normal((1, 1, 16)), (2, 37, 1))
+    for beta in (-2.0, 0.0, 1.0):
+        r = oracle.route(qr, kr, beta, want_shat=True)
+        assert r["kept"].sum() == 0
+        assert np.all(r["sigma"] == 0.0)
+        assert np.array_equal(r["mu"], r["shat"][:, :, 0]) and np.array_equal(r["tau"], r["mu"])
+    assert oracle.route(qr, kr, float("-inf"))["kept"].min() == 37
     # a non-constant row: beta=-inf keeps all, beta=+inf keeps none
     kb2 = rand((H, N, d), 14).astype(np.float64)
     assert oracle.route(qbar, kb2, float("-inf"))["kept"].min() == N
