@@ -13,7 +13,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsol.so")
 SOURCES = [os.path.join(CSRC, f) for f in
            ("sol_pool_route.hip", "sol_sweep.hip", "sol_f32.hip", "sol_api.hip")]
+HEADERS = [os.path.join(CSRC, "sol_device.h"), os.path.join(CSRC, "sol_launch.h"),
+           os.path.join(INCLUDE, "sol.h")]
 ARCH = "gfx950"
+DIGEST = LIB + ".srcdigest"  # digest of the sources and flags LIB was built from
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -22,6 +25,36 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+
+
+def source_digest(extra=()) -> str:
+    """sha256 over the library's sources, headers and compiler flags."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in SOURCES + HEADERS:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + b"\0" + fh.read() + b"\0")
+    h.update(" ".join(HIPCC_FLAGS + list(extra)).encode())
+    return h.hexdigest()
+
+
+def built_digest():
+    """The digest recorded when LIB was built (None if there is none)."""
+    try:
+        with open(DIGEST) as fh:
+            return fh.read().strip()
+    except OSError:
+        return None
+
+
+def check_current():
+    """Raise unless LIB exists and was built from the sources as they are now."""
+    if not os.path.exists(LIB):
+        raise RuntimeError(f"{LIB} is missing: build it with "
+                           "`python -m block_sparse_attention_23_amd.build` (hipcc, gfx950)")
+    if built_digest() != source_digest():
+        raise RuntimeError(f"{LIB} is stale: it was not built from the current sources "
+                           "(rebuild with `python -m block_sparse_attention_23_amd.build`)")
 
 
 def hipcc():
@@ -42,6 +75,9 @@ def build(verbose: bool = False, extra=()) -> str:
     if verbose and errs.strip():
         print(errs, file=sys.stderr)
     os.replace(LIB + ".tmp", LIB)
+    with open(DIGEST + ".tmp", "w") as fh:
+        fh.write(source_digest(extra) + "\n")
+    os.replace(DIGEST + ".tmp", DIGEST)
     return LIB
 
 

@@ -53,10 +53,15 @@ def _load(path):
 
 
 def lib():
+    """The loaded oracle library, built here if it is missing; raises if the
+    library present was built from another version of sol_oracle.c."""
     global _LIB
     if _LIB is None:
         if not os.path.exists(_build.LIB):
             _build.build()
+        if _build.built_digest() != _build.source_digest():
+            raise RuntimeError(f"{_build.LIB} is stale: it was not built from the current "
+                               "sol_oracle.c (rebuild with `python -m oracle.build`)")
         _LIB = _load(_build.LIB)
     return _LIB
 

@@ -154,3 +154,26 @@ def test_variant_rejects_bad_flags_and_fractions(lib):
         if i == 8:
             bad[9] = 2  # the fraction matters for the fixed budget only
         assert lib.sol_attn_fwd_variant(*bad) == want, (i, val)
+
+
+def test_library_built_from_current_sources(lib):
+    """build() records the digest of the sources and flags it compiled; the
+    library in the tree matches the sources in the tree."""
+    assert build.built_digest() == build.source_digest()
+
+
+def test_stale_library_is_refused(monkeypatch):
+    """A library built from other sources (digest mismatch) is not loaded."""
+    monkeypatch.setattr(binding, "_LIB", None)
+    monkeypatch.setattr(build, "source_digest", lambda extra=(): "0" * 64)
+    with pytest.raises(RuntimeError, match="stale"):
+        binding.lib()
+
+
+def test_stale_oracle_is_refused(monkeypatch):
+    import oracle
+    from oracle import build as obuild
+    monkeypatch.setattr(oracle, "_LIB", None)
+    monkeypatch.setattr(obuild, "source_digest", lambda: "0" * 64)
+    with pytest.raises(RuntimeError, match="stale"):
+        oracle.lib()
