@@ -42,7 +42,7 @@ int check_tensors(const void* q, const void* k, const void* v, const void* out, 
 //   queues           : int32[8]           sweep work counters
 //   kbar_bf, vsum_bf : bf16 [H][N][d]     MFMA operands of the approximate path
 //   sel              : u32  [H][N][W]     selection bits, W = ceil(N / 32)
-//   mom              : fp32 [H][d + d*d]  key moments (routing rows longer than LDS holds)
+//   mom              : fp32 [H][2d + d*d] key moments (routing rows longer than LDS holds)
 struct Workspace {
     float* qbar;
     float* kbar;
@@ -63,7 +63,7 @@ Workspace carve(void* base, int H, int L, int d, int B) {
     const size_t taub = align_up(sizeof(float) * (size_t)H * N);
     const size_t qb = align_up(sizeof(int) * 8);
     const size_t selb = align_up(sizeof(uint32_t) * (size_t)H * N * ((N + 31) / 32));
-    const size_t momb = align_up(sizeof(float) * (size_t)H * ((size_t)d + (size_t)d * d));
+    const size_t momb = align_up(sizeof(float) * (size_t)H * (2 * (size_t)d + (size_t)d * d));
     char* p = static_cast<char*>(base);
     Workspace w;
     size_t off = 0;

@@ -87,7 +87,10 @@ __global__ void __launch_bounds__(256) pool_kernel(const T* __restrict__ q, cons
         red[2][rg][ch * VEC + e] = av[e];
     }
     __syncthreads();
-    const float inv_n = 1.0f / static_cast<float>(n);
+    // means by a correctly rounded division: a block of equal tokens pools
+    // to exactly their value (their sum n x is exact), also when n is not a
+    // power of two
+    const float fn = static_cast<float>(n);
     for (int x = tid; x < 3 * D; x += 256) {
         const int which = x / D, col = x % D;
         float s = 0.0f;
@@ -95,9 +98,9 @@ __global__ void __launch_bounds__(256) pool_kernel(const T* __restrict__ q, cons
         for (int r = 0; r < RG; ++r) s += red[which][r][col];
         const size_t o = (size_t)item * D + col;
         if (which == 0) {
-            qbar[o] = s * inv_n;
+            qbar[o] = s / fn;
         } else if (which == 1) {
-            const float m = s * inv_n;
+            const float m = s / fn;
             kbar[o] = m;
             if (kbar_bf) kbar_bf[o] = f32_to_bf16_bits(m);
         } else {
@@ -289,11 +292,23 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
     // fixed order, then a butterfly whose result every lane shares)
     for (int r = wave; r < nr; r += 4) {
         const float* row = rows + r * N;
-        float part = 0.0f;
-        for (int j = lane; j < N; j += 64) part += row[j];
+        float part = 0.0f, lo = INFINITY, hi = -INFINITY;
+        for (int j = lane; j < N; j += 64) {
+            part += row[j];
+            lo = fminf(lo, row[j]);
+            hi = fmaxf(hi, row[j]);
+        }
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-        const float mu = part / static_cast<float>(N);
+        for (int off = 32; off >= 1; off >>= 1) {
+            part += __shfl_xor(part, off);
+            lo = fminf(lo, __shfl_xor(lo, off));
+            hi = fmaxf(hi, __shfl_xor(hi, off));
+        }
+        // a constant row (every score equal, e.g. N = 1 or equal pooled
+        // keys) has sigma = 0 and tau = its value exactly: no score is
+        // strictly above it, which the fp32 mean of equal terms need not show
+        const bool flat = lo == hi;
+        const float mu = flat ? lo : part / static_cast<float>(N);
         float pv = 0.0f;
         for (int j = lane; j < N; j += 64) {
             const float dlt = row[j] - mu;
@@ -301,7 +316,7 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
         }
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) pv += __shfl_xor(pv, off);
-        const float sigma = sqrtf(fmaxf(pv / static_cast<float>(N), 0.0f));
+        const float sigma = flat ? 0.0f : sqrtf(fmaxf(pv / static_cast<float>(N), 0.0f));
         float tau;
         if (tau_in) tau = tau_in[(size_t)h * N + i0 + r];  // thresholds given by the caller
         else if (isinf(beta)) tau = beta;                  // -inf: every block exact; +inf: none
@@ -325,14 +340,23 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
 }
 
 // ============================================================================
-// key moments (Eq. (5)): per head the mean of the pooled keys
-// mbar = (1/N) sum_j kbar_j and their second moments
-// C = (1/N) sum_j kbar_j kbar_j^T, from which the proxy row's population
-// mean and variance follow without forming the row:
-// mu_i = c qbar_i . mbar and sigma_i^2 = c^2 qbar_i C qbar_i^T - mu_i^2.
-// Workgroup (h, bi, bj) forms the 32x32 block (bi, bj) of C (and, for
-// bj = 0, 32 entries of mbar), summing over j in a fixed order.  Per head:
-// mbar, then C row-major (D + D*D floats).
+// key moments (Eq. (5)), centred: per head the mean pooled key and the
+// covariance of the pooled keys about it, from which the proxy row's
+// population mean and variance follow without forming the row:
+//     mbar = (1/N) sum_j kbar_j,   Cov = (1/N) sum_j (kbar_j - mbar)(kbar_j - mbar)^T
+//     mu_i = c qbar_i . mbar,      sigma_i^2 = c^2 qbar_i Cov qbar_i^T.
+// This is Eq. (5)'s moment form with the mean taken out before the products
+// are summed (its C minus mbar mbar^T), so sigma_i^2 is a sum of
+// non-negative terms and no large, nearly equal numbers are subtracted when
+// the keys share a large common component.  To keep the centring itself
+// exact in fp32 for keys that are all equal, the keys are first shifted by
+// the head's first pooled key: y_j = kbar_j - kbar_0 (exactly 0 for a key
+// equal to kbar_0), ybar = (1/N) sum_j y_j, and Cov is summed from
+// y_j - ybar; then mbar = kbar_0 + ybar.
+// Workgroup (h, bi, bj) forms the 32x32 block (bi, bj) of Cov: a first pass
+// takes ybar for its 64 columns (every workgroup sums a column in the same
+// order, so all of them agree), a second the centred products.  Per head:
+// kbar_0 (D floats), ybar (D), then Cov row-major (D*D).
 // ============================================================================
 template <int D>
 __global__ void __launch_bounds__(256) key_moments_kernel(const float* __restrict__ kbar, int N,
@@ -340,18 +364,38 @@ __global__ void __launch_bounds__(256) key_moments_kernel(const float* __restric
     constexpr int NBK = D / 32;
     __shared__ float ka[64][33];
     __shared__ float kb[64][33];
+    __shared__ float k0[64];      // kbar_0 at columns 32 bi + e (e < 32), 32 bj + e - 32
+    __shared__ float part[4][64];  // partial column sums of y
+    __shared__ float ym[64];      // ybar at the same columns
     const int h = blockIdx.x / (NBK * NBK);
     const int bi = (blockIdx.x / NBK) % NBK, bj = blockIdx.x % NBK;
     const int tid = threadIdx.x, a = tid >> 3, b4 = (tid & 7) * 4;
     const float* kh = kbar + (size_t)h * N * D;
+    auto col_of = [&](int e) { return e < 32 ? 32 * bi + e : 32 * bj + e - 32; };
+    if (tid < 64) k0[tid] = kh[col_of(tid)];
+    __syncthreads();
+
+    // pass 1: ybar.  Thread (p, e) sums rows j = p, p + 4, ... of column e.
+    {
+        const int e = tid & 63, p = tid >> 6;
+        const int col = col_of(e);
+        const float base = k0[e];
+        float s = 0.0f;
+        for (int j = p; j < N; j += 4) s += kh[(size_t)j * D + col] - base;
+        part[p][e] = s;
+    }
+    __syncthreads();
+    if (tid < 64) ym[tid] = ((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid])) / static_cast<float>(N);
+    __syncthreads();
+
+    // pass 2: Cov block (bi, bj) from the centred keys
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    float macc = 0.0f;
     for (int j0 = 0; j0 < N; j0 += 64) {
         __syncthreads();
         for (int x = tid; x < 64 * 32; x += 256) {
             const int jj = x >> 5, e = x & 31, j = j0 + jj;
-            ka[jj][e] = j < N ? kh[(size_t)j * D + 32 * bi + e] : 0.0f;
-            kb[jj][e] = j < N ? kh[(size_t)j * D + 32 * bj + e] : 0.0f;
+            ka[jj][e] = j < N ? (kh[(size_t)j * D + 32 * bi + e] - k0[e]) - ym[e] : 0.0f;
+            kb[jj][e] = j < N ? (kh[(size_t)j * D + 32 * bj + e] - k0[32 + e]) - ym[32 + e] : 0.0f;
         }
         __syncthreads();
 #pragma unroll 8
@@ -359,14 +403,16 @@ __global__ void __launch_bounds__(256) key_moments_kernel(const float* __restric
             const float x = ka[jj][a];
 #pragma unroll
             for (int cc = 0; cc < 4; ++cc) acc[cc] = __builtin_fmaf(x, kb[jj][b4 + cc], acc[cc]);
-            macc += x;
         }
     }
     const float inv = 1.0f / static_cast<float>(N);
-    float* mh = mom + (size_t)h * (D + D * D);
+    float* mh = mom + (size_t)h * (2 * D + D * D);
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) mh[D + (32 * bi + a) * D + 32 * bj + b4 + cc] = acc[cc] * inv;
-    if (bj == 0 && b4 == 0) mh[32 * bi + a] = macc * inv;
+    for (int cc = 0; cc < 4; ++cc) mh[2 * D + (32 * bi + a) * D + 32 * bj + b4 + cc] = acc[cc] * inv;
+    if (bj == 0 && tid < 32) {
+        mh[32 * bi + tid] = k0[tid];
+        mh[D + 32 * bi + tid] = ym[tid];
+    }
 }
 
 // ============================================================================
@@ -387,7 +433,8 @@ __global__ void __launch_bounds__(256) route_moments_kernel(
     constexpr int R = 16;
     extern __shared__ uint16_t bits16[];  // [R][NKT]: the decisions on 16-key tile kt of row r
     __shared__ float qs[R][D + 1];
-    __shared__ float tau_s[R];
+    __shared__ float tau_s[R];    // the thresholds reported
+    __shared__ float tau_cmp[R];  // the thresholds compared with (+inf: select none)
     const int h = blockIdx.x / groups_per_head;
     const int i0 = (blockIdx.x % groups_per_head) * R;
     const int nr = min(R, N - i0);
@@ -401,12 +448,20 @@ __global__ void __launch_bounds__(256) route_moments_kernel(
     __syncthreads();
 
     // thresholds: wave w takes rows 4w .. 4w+3, lane l the columns l + 64 m of
-    // v = qbar_r C, then e_r = v . qbar_r and qbar_r . mbar by butterflies
+    // v = qbar_r Cov, then e_r = v . qbar_r (= sigma_r^2 / c^2) and
+    // qbar_r . mbar = qbar_r . kbar_0 + qbar_r . ybar by butterflies.
+    // sigma_r = 0 (the pooled keys all equal, or qbar_r orthogonal to their
+    // spread: every s_rj is then mu_r in exact arithmetic) selects no block:
+    // none is strictly above tau_r = mu_r.
     if (tau_in || isinf(beta)) {
-        if (tid < R) tau_s[tid] = tau_in ? tau_in[(size_t)h * N + min(i0 + tid, N - 1)] : beta;
+        if (tid < R) {
+            tau_s[tid] = tau_in ? tau_in[(size_t)h * N + min(i0 + tid, N - 1)] : beta;
+            tau_cmp[tid] = tau_s[tid];
+        }
     } else {
         constexpr int CPL = D / 64;
-        const float* mh = mom + (size_t)h * (D + D * D);
+        const float* mh = mom + (size_t)h * (2 * D + D * D);
+        const float* cov = mh + 2 * D;
         float v[4][CPL];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
@@ -416,7 +471,7 @@ __global__ void __launch_bounds__(256) route_moments_kernel(
         for (int dp = 0; dp < D; ++dp) {
             float crow[CPL];
 #pragma unroll
-            for (int m = 0; m < CPL; ++m) crow[m] = mh[D + dp * D + lane + 64 * m];
+            for (int m = 0; m < CPL; ++m) crow[m] = cov[dp * D + lane + 64 * m];
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const float qd = qs[4 * wave + rr][dp];
@@ -427,22 +482,25 @@ __global__ void __launch_bounds__(256) route_moments_kernel(
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const int r = 4 * wave + rr;
-            float e = 0.0f, mu = 0.0f;
+            float e = 0.0f, mu0 = 0.0f, mu1 = 0.0f;
 #pragma unroll
             for (int m = 0; m < CPL; ++m) {
                 const int col = lane + 64 * m;
                 e = __builtin_fmaf(qs[r][col], v[rr][m], e);
-                mu = __builtin_fmaf(qs[r][col], mh[col], mu);
+                mu0 = __builtin_fmaf(qs[r][col], mh[col], mu0);
+                mu1 = __builtin_fmaf(qs[r][col], mh[D + col], mu1);
             }
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) {
                 e += __shfl_xor(e, off);
-                mu += __shfl_xor(mu, off);
+                mu0 += __shfl_xor(mu0, off);
+                mu1 += __shfl_xor(mu1, off);
             }
             if (lane == 0) {
-                const float m_ = c * mu;
-                const float var = fmaxf(c * c * e - m_ * m_, 0.0f);
-                tau_s[r] = __builtin_fmaf(beta, sqrtf(var), m_);
+                const float m_ = c * (mu0 + mu1);
+                const float var = c * c * fmaxf(e, 0.0f);
+                tau_s[r] = var > 0.0f ? __builtin_fmaf(beta, sqrtf(var), m_) : m_;
+                tau_cmp[r] = var > 0.0f ? tau_s[r] : INFINITY;
             }
         }
     }
@@ -458,7 +516,7 @@ __global__ void __launch_bounds__(256) route_moments_kernel(
     const float* kh = kbar + (size_t)h * N * D;
     float tr[4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) tr[x] = tau_s[4 * g + x];
+    for (int x = 0; x < 4; ++x) tr[x] = tau_cmp[4 * g + x];
     auto kload = [&](int kt, float (&kv)[QD]) __attribute__((always_inline)) {
         const float4* src = reinterpret_cast<const float4*>(kh + (size_t)min(kt * 16 + l16, N - 1) * D + g * QD);
 #pragma unroll

@@ -224,3 +224,26 @@ def grid_inputs(H: int, grid: Tuple[int, int, int], d: int, seed: int, dtype: st
     w = Workload(f"grid{grid}", H=H, d=d, B=64, dtype=dtype, betas=(), seed=seed,
                  grids=(grid,), truncate=truncate)
     return generate(w)
+
+
+def shifted_inputs(inp: Inputs, q_shift: Optional[np.ndarray] = None,
+                   k_shift: Optional[np.ndarray] = None,
+                   k_const: Optional[np.ndarray] = None) -> Inputs:
+    """Edge-case inputs built from ``inp``: ``q_shift`` / ``k_shift`` (length d)
+    are added to every query / key token, or every key token is replaced by
+    ``k_const``; the result is re-rounded to the workload's dtype.  A common
+    key component makes every proxy row's mean large against its spread; equal
+    keys make every proxy row constant."""
+    w = inp.workload
+    q, k = inp.q.copy(), inp.k.copy()
+    if q_shift is not None:
+        q += np.asarray(q_shift, dtype=np.float32)
+    if k_shift is not None:
+        k += np.asarray(k_shift, dtype=np.float32)
+    if k_const is not None:
+        k[...] = np.asarray(k_const, dtype=np.float32)
+    if w.dtype == "bf16":
+        qb, qv = round_bf16(q)
+        kb, kv = round_bf16(k)
+        return Inputs(w, inp.heads, qv, kv, inp.v, (qb, kb, inp.v_bits))
+    return Inputs(w, inp.heads, q, k, inp.v, (None, None, None))

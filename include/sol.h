@@ -52,7 +52,7 @@ typedef enum {
  * per-query-block thresholds (H*N fp32), the scheduler's queue counters, bf16
  * copies of the pooled keys and summed values (2 x H*N*d bf16), the
  * selection bits (H*N*ceil(N/32) uint32) and the key moments
- * (H*(d + d*d) fp32).  0 for invalid shapes.
+ * (H*(2d + d*d) fp32).  0 for invalid shapes.
  */
 size_t sol_workspace_bytes(int H, int L, int d, int B);
 
@@ -86,9 +86,13 @@ int sol_pool(const void* q, const void* k, const void* v,
  *              256-byte aligned (scratch; missing or small: SOL_EWORKSPACE).
  * For N <= 1280 each row s_i. is held on chip and mu_i, sigma_i are its
  * two-pass statistics.  For longer rows mu_i and sigma_i come from the key
- * moments of Eq. (5), mu_i = c qbar_i . mbar and sigma_i^2 = c^2 qbar_i C
- * qbar_i^T - mu_i^2 with mbar = (1/N) sum_j kbar_j and C = (1/N) sum_j
- * kbar_j kbar_j^T (computed into the workspace), equal in exact arithmetic.
+ * moments of Eq. (5), taken about the mean pooled key (equal in exact
+ * arithmetic): mu_i = c qbar_i . mbar and sigma_i^2 = c^2 qbar_i Cov qbar_i^T
+ * with mbar = (1/N) sum_j kbar_j and Cov = (1/N) sum_j (kbar_j - mbar)
+ * (kbar_j - mbar)^T (computed into the workspace; no subtraction of nearly
+ * equal terms when the keys share a large common component).  A row whose
+ * sigma_i is 0 (all its scores equal) keeps no block: none is strictly above
+ * tau_i = mu_i.
  * The counts and bits are those the forward pass uses (the same kernels
  * form every s_ij, by fp32 matrix instructions; both sweeps take their
  * decisions from these bits).
