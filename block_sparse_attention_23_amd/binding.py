@@ -53,13 +53,11 @@ def library_path():
 
 
 def lib():
-    """The loaded libsol.so; raises if it has not been built."""
+    """The loaded libsol.so; raises if it is missing or was built from other
+    sources than those in the tree."""
     global _LIB
     if _LIB is None:
-        if not os.path.exists(_build.LIB):
-            raise RuntimeError(
-                f"{_build.LIB} is missing: build it with "
-                "`python -m block_sparse_attention_23_amd.build` (hipcc, gfx950)")
+        _build.check_current()  # missing or stale (built from other sources): raise
         L = ctypes.CDLL(_build.LIB)
         for name, (res, args) in _FUNCS.items():
             f = getattr(L, name)
@@ -103,6 +101,16 @@ def _stream_ptr(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream, device):
+    """Context in which tensors the binding creates are allocated: the stream
+    the kernels run on.  The caching allocator then hands a freed block
+    (a temporary workspace, say) to later work on that same stream only, so
+    no other stream can reuse it while those kernels still read or write it."""
+    with torch.cuda.device(device):
+        s = stream if stream is not None else torch.cuda.current_stream(device)
+    return torch.cuda.stream(s)
+
+
 def nblocks(L, B):
     return (L + B - 1) // B
 
@@ -123,7 +131,8 @@ def pool(q, k, v, B, outs=None, stream=None):
     H, L, d = _tokens(q, k, v)
     N = nblocks(L, B)
     if outs is None:
-        outs = [torch.empty((H, N, d), dtype=torch.float32, device=q.device) for _ in range(3)]
+        with _on(stream, q.device):
+            outs = [torch.empty((H, N, d), dtype=torch.float32, device=q.device) for _ in range(3)]
     with torch.cuda.device(q.device):
         _check("sol_pool", lib().sol_pool(q.data_ptr(), k.data_ptr(), v.data_ptr(), H, L, d, B,
                                           _dtype_code(q), outs[0].data_ptr(), outs[1].data_ptr(),
@@ -137,12 +146,13 @@ def route(qbar, kbar, L, B, beta, tau=None, kept=None, sel_bits=None, workspace=
     H, N, d = qbar.shape
     if not (qbar.is_cuda and kbar.is_cuda):
         raise ValueError("pooled tensors must live on the GPU")
-    if tau is None:
-        tau = torch.empty((H, N), dtype=torch.float32, device=qbar.device)
-    if kept is None:
-        kept = torch.empty((H, N), dtype=torch.int32, device=qbar.device)
-    if workspace is None:
-        workspace = alloc_workspace(H, L, d, B, qbar.device)
+    with _on(stream, qbar.device):
+        if tau is None:
+            tau = torch.empty((H, N), dtype=torch.float32, device=qbar.device)
+        if kept is None:
+            kept = torch.empty((H, N), dtype=torch.int32, device=qbar.device)
+        if workspace is None:
+            workspace = alloc_workspace(H, L, d, B, qbar.device)
     with torch.cuda.device(qbar.device):
         _check("sol_route", lib().sol_route(qbar.data_ptr(), kbar.data_ptr(), H, L, d, B,
                                             float(beta), tau.data_ptr(), kept.data_ptr(),
@@ -162,10 +172,11 @@ def sweep(q, k, v, qbar, kbar, vsum, tau, B, out=None, workspace=None, sel_bits=
     """The fused exact/approximate sweep given pooled tensors and thresholds
     (and, optionally, the decisions sol_route wrote for them)."""
     H, L, d = _tokens(q, k, v)
-    if out is None:
-        out = torch.empty_like(q)
-    if workspace is None:
-        workspace = alloc_workspace(H, L, d, B, q.device)
+    with _on(stream, q.device):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = alloc_workspace(H, L, d, B, q.device)
     with torch.cuda.device(q.device):
         _check("sol_sweep", lib().sol_sweep(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), qbar.data_ptr(), kbar.data_ptr(),
@@ -181,12 +192,17 @@ def attn_fwd(q, k, v, B, beta, out=None, kept=None, workspace=None, stream=None,
     (out, kept_counts, sel_mask [H][N][ceil(N/32)] int32 bits, tau [H][N])."""
     H, L, d = _tokens(q, k, v)
     N = nblocks(L, B)
-    if out is None:
-        out = torch.empty_like(q)
-    if kept is None:
-        kept = torch.empty((H, N), dtype=torch.int32, device=q.device)
-    if workspace is None:
-        workspace = alloc_workspace(H, L, d, B, q.device)
+    with _on(stream, q.device):
+        if out is None:
+            out = torch.empty_like(q)
+        if kept is None:
+            kept = torch.empty((H, N), dtype=torch.int32, device=q.device)
+        if workspace is None:
+            workspace = alloc_workspace(H, L, d, B, q.device)
+        if debug:
+            W = (N + 31) // 32
+            mask = torch.zeros((H, N, W), dtype=torch.int32, device=q.device)
+            tau = torch.empty((H, N), dtype=torch.float32, device=q.device)
     args = [q.data_ptr(), k.data_ptr(), v.data_ptr(), H, L, d, B, float(beta), _dtype_code(q),
             out.data_ptr(), kept.data_ptr(), workspace.data_ptr(), workspace.numel(),
             _stream_ptr(stream, q.device)]
@@ -194,9 +210,6 @@ def attn_fwd(q, k, v, B, beta, out=None, kept=None, workspace=None, stream=None,
         if not debug:
             _check("sol_attn_fwd", lib().sol_attn_fwd(*args))
             return out, kept
-        W = (N + 31) // 32
-        mask = torch.zeros((H, N, W), dtype=torch.int32, device=q.device)
-        tau = torch.empty((H, N), dtype=torch.float32, device=q.device)
         _check("sol_attn_fwd_dbg", lib().sol_attn_fwd_dbg(*args, mask.data_ptr(), tau.data_ptr()))
         return out, kept, mask, tau
 
@@ -209,15 +222,16 @@ def attn_fwd_variant(q, k, v, B, beta, keep_frac=0.0, drop_approx=False, topk=Fa
     threshold.  Returns (out, kept_counts, sel_mask bits, tau)."""
     H, L, d = _tokens(q, k, v)
     N = nblocks(L, B)
-    if out is None:
-        out = torch.empty_like(q)
-    if kept is None:
-        kept = torch.empty((H, N), dtype=torch.int32, device=q.device)
-    if workspace is None:
-        workspace = alloc_workspace(H, L, d, B, q.device)
+    with _on(stream, q.device):
+        if out is None:
+            out = torch.empty_like(q)
+        if kept is None:
+            kept = torch.empty((H, N), dtype=torch.int32, device=q.device)
+        if workspace is None:
+            workspace = alloc_workspace(H, L, d, B, q.device)
+        mask = torch.zeros((H, N, (N + 31) // 32), dtype=torch.int32, device=q.device)
+        tau = torch.empty((H, N), dtype=torch.float32, device=q.device)
     flags = (SOL_DROP_APPROX if drop_approx else 0) | (SOL_TOPK if topk else 0)
-    mask = torch.zeros((H, N, (N + 31) // 32), dtype=torch.int32, device=q.device)
-    tau = torch.empty((H, N), dtype=torch.float32, device=q.device)
     with torch.cuda.device(q.device):
         _check("sol_attn_fwd_variant", lib().sol_attn_fwd_variant(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), H, L, d, B, float(beta), float(keep_frac),
@@ -230,7 +244,8 @@ def attn_dense(q, k, v, out=None, stream=None):
     """Dense softmax(q k^T / sqrt(d)) v on the same tile machinery."""
     H, L, d = _tokens(q, k, v)
     if out is None:
-        out = torch.empty_like(q)
+        with _on(stream, q.device):
+            out = torch.empty_like(q)
     with torch.cuda.device(q.device):
         _check("sol_attn_dense", lib().sol_attn_dense(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                                       H, L, d, _dtype_code(q), out.data_ptr(),

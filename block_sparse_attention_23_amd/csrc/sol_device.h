@@ -113,7 +113,7 @@ __device__ __forceinline__ int claim_item(int* queues, int H, int N) {
         const int nx = hi - lo;
         if (nx == 0) continue;
         const int kk = atomicAdd(&queues[x], 1);
-        if (kk < H * nx) return (kk / nx) * N + lo + (kk % nx);
+        if (kk >= 0 && kk < H * nx) return (kk / nx) * N + lo + (kk % nx);
     }
     return -1;
 }

@@ -373,11 +373,13 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             return DENSE ? ((all_part << S::PS) | (uint32_t)(t / S::SUB))
                          : (uint32_t)__builtin_amdgcn_readfirstlane((int)raw);
         };
-        // (approx?, part, row0 of the tile in its source) of tile t
+        // (approx?, part, row0 of the tile in its source) of tile t; a B = 32
+        // pair entry holds two key blocks instead of an index (row0 = 0,
+        // unused: its rows come from pair_of)
         auto decode = [&](uint32_t d, int t, bool& approx, uint32_t& part, int& row0) {
             approx = (d & kApprox) != 0;
             part = (d >> S::PS) & ((1u << S::PB) - 1u);
-            row0 = (int)(d & ((1u << S::PS) - 1u)) * S::TB + (t % S::SUB) * 64;
+            row0 = (S::KPT == 2 && !approx) ? 0 : (int)(d & ((1u << S::PS) - 1u)) * S::TB + (t % S::SUB) * 64;
         };
         // (B = 32 exact entries) the pair's key blocks
         auto pair_of = [&](uint32_t d, int& j1, int& j2, bool& has2) {
