@@ -77,17 +77,16 @@ def _take(a, hs):
     return a if hs == list(range(a.shape[0])) else a[hs]
 
 
-def run_and_check(inp, B, beta, rows=None, sel_heads=None):
-    """Full check of sol_attn_fwd_dbg on `inp` (all heads run on the GPU).
+def check_result(inp, B, beta, out, kept, mask, rows=None, sel_heads=None):
+    """Check GPU results already computed for `inp` (all heads): `out`
+    [H][L][d], `kept` [H][N] and the kernel's own decision bits `mask`
+    [H][N][ceil(N/32)] (device tensors).
 
     rows: None = compare every output row; else an [n][2] array of (h, r)
     with h indexing `sel_heads` (or all heads).
     sel_heads: heads whose selection and outputs are checked (None = all)."""
     w = inp.workload
-    q, k, v = to_device(inp)
-    out, kept, mask, tau = binding.attn_fwd(q, k, v, B, beta, debug=True)
-    torch.cuda.synchronize()
-    H, L, d = q.shape
+    H, L, d = out.shape
     N = (L + B - 1) // B
     gsel = binding.unpack_mask(mask, N)
     gkept = kept.cpu().numpy()
@@ -104,5 +103,15 @@ def run_and_check(inp, B, beta, rows=None, sel_heads=None):
         ridx = torch.tensor(rows[:, 1], device=out.device, dtype=torch.long)
         got = out[hidx, ridx].float().cpu().numpy()
     stats = check_output(got, ref, w.dtype)
-    stats.update(flips=flips, kept_frac=float(gsel.mean()), oracle_kept_frac=okept)
+    stats.update(flips=flips, kept_frac=float(gsel.mean()), oracle_kept_frac=okept,
+                 compared=int(got.size))
     return stats
+
+
+def run_and_check(inp, B, beta, rows=None, sel_heads=None, workspace=None):
+    """Full check of sol_attn_fwd_dbg on `inp` (all heads run on the GPU);
+    rows and sel_heads as in check_result."""
+    q, k, v = to_device(inp)
+    out, kept, mask, tau = binding.attn_fwd(q, k, v, B, beta, debug=True, workspace=workspace)
+    torch.cuda.synchronize()
+    return check_result(inp, B, beta, out, kept, mask, rows=rows, sel_heads=sel_heads)

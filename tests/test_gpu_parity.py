@@ -11,7 +11,7 @@ import oracle
 from block_sparse_attention_23_amd import binding
 from block_sparse_attention_23_amd import inputs as gen
 
-from .parity import TOL, block_rows, check_output, run_and_check, to_device
+from .parity import block_rows, check_output, check_result, run_and_check, to_device
 
 pytestmark = pytest.mark.gpu
 INF = math.inf
@@ -64,7 +64,7 @@ def test_forward_bf16_unstructured(beta):
 
 @pytest.mark.parametrize("beta", [-INF, 0.0, 1.0, INF])
 @pytest.mark.parametrize("d,B,L", [(64, 64, 1024), (128, 64, 333), (64, 128, 1000), (128, 32, 1000),
-                                   (64, 32, 333)])
+                                   (64, 32, 333), (128, 128, 1000), (128, 128, 256)])
 def test_forward_fp32(d, B, L, beta):
     inp = grid_inp(2, L, d, "fp32", seed=5)
     run_and_check(inp, B, beta)
@@ -120,38 +120,73 @@ def test_deterministic_across_runs():
 
 
 def test_outputs_stay_inside_their_buffers():
-    """Guard bands around out and kept_counts are untouched."""
+    """Guard bands around out, kept_counts and the decision bits are
+    untouched, and the values written inside them pass the parity rule."""
     inp = grid_inp(2, 1000, 128, "bf16", seed=7)
     q, k, v = to_device(inp)
     H, L, d = q.shape
     N = (L + 63) // 64
+    W = binding.sel_words(N)
     guard = 4096
     big = torch.full((2 * guard + H * L * d,), 1234.0, dtype=torch.bfloat16, device="cuda")
     out = big[guard:guard + H * L * d].view(H, L, d)
     kbig = torch.full((2 * 256 + H * N,), -77, dtype=torch.int32, device="cuda")
     kept = kbig[256:256 + H * N].view(H, N)
-    binding.attn_fwd(q, k, v, 64, 1.0, out=out, kept=kept)
+    mbig = torch.full((2 * 256 + H * N * W,), -5, dtype=torch.int32, device="cuda")
+    mask = mbig[256:256 + H * N * W].view(H, N, W)
+    ws = binding.alloc_workspace(H, L, d, 64, q.device)
+    st = binding.lib().sol_attn_fwd_dbg(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), H, L, d, 64, 1.0, binding.SOL_BF16,
+        out.data_ptr(), kept.data_ptr(), ws.data_ptr(), ws.numel(),
+        binding._stream_ptr(None, q.device), mask.data_ptr(), None)
+    assert st == 0
     torch.cuda.synchronize()
     assert torch.all(big[:guard] == 1234.0) and torch.all(big[guard + H * L * d:] == 1234.0)
     assert torch.all(kbig[:256] == -77) and torch.all(kbig[256 + H * N:] == -77)
-    ref, r = oracle.attention(inp.q, inp.k, inp.v, 64, 1.0)
-    assert np.array_equal(kept.cpu().numpy() >= 0, np.ones((H, N), bool))
+    assert torch.all(mbig[:256] == -5) and torch.all(mbig[256 + H * N * W:] == -5)
+    s = check_result(inp, 64, 1.0, out, kept, mask)
+    assert s["compared"] == H * L * d
 
 
 def test_workspace_reuse_across_shapes():
-    """One workspace sized for the larger call serves a smaller call next."""
+    """One workspace sized for the larger call serves a smaller call next
+    (its stale contents from the larger call do not leak into the result):
+    selection with the flip rule and every output element."""
     big = grid_inp(2, 2000, 128, "bf16", seed=8)
     small = grid_inp(1, 300, 128, "bf16", seed=9)
     ws = binding.alloc_workspace(2, 2000, 128, 64, "cuda")
     qb, kb, vb = to_device(big)
-    qs, ks, vs = to_device(small)
     binding.attn_fwd(qb, kb, vb, 64, 1.0, workspace=ws)
-    o_small, _ = binding.attn_fwd(qs, ks, vs, 64, 1.0, workspace=ws)
+    s = run_and_check(small, 64, 1.0, workspace=ws)
+    assert s["compared"] == 300 * 128
+    s = run_and_check(big, 64, 1.0, workspace=ws)
+    assert s["compared"] == 2 * 2000 * 128
+
+
+def test_side_stream_without_workspace_survives_default_stream_reuse():
+    """attn_fwd on a side stream with no caller workspace: the binding's
+    temporary workspace belongs to the side stream, so a same-sized buffer
+    that the default stream allocates and clears right after the call does
+    not share its memory while the side-stream kernels still use it."""
+    inp = grid_inp(8, 16000, 128, "bf16", seed=18)
+    q, k, v = to_device(inp)
+    H, L, d = q.shape
+    ref_out, ref_kept = binding.attn_fwd(q, k, v, 64, 1.0)
     torch.cuda.synchronize()
-    ref, _ = oracle.attention(small.q, small.k, small.v, 64, 1.0)
-    # selection is the oracle's here unless a flip occurs; compare loosely on the mean
-    err = np.abs(o_small.float().cpu().numpy() - ref)
-    assert err.mean() <= TOL["bf16"][1]
+    n_ws = binding.workspace_bytes(H, L, d, 64)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        out = torch.empty_like(q)
+        kept = torch.empty_like(ref_kept)
+    side.synchronize()
+    for _ in range(3):
+        binding.attn_fwd(q, k, v, 64, 1.0, out=out, kept=kept, stream=side)
+        junk = torch.empty(n_ws, dtype=torch.uint8, device=q.device)
+        junk.zero_()
+        del junk
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref_out) and torch.equal(kept, ref_kept)
 
 
 @pytest.mark.parametrize("dtype,d,B,L", [("bf16", 128, 64, 1000), ("bf16", 64, 128, 700),

@@ -1,19 +1,23 @@
 """HIP path vs the fp64 oracle at the workloads' full sizes, in the launch
 configuration the benchmark times (every head and query block runs on the
-GPU).  Selection parity is checked for every (h, i, j); outputs are compared
-element by element on sampled query blocks that the oracle computes one by
-one, including the first, middle and ragged last block of first, middle and
-last heads."""
+GPU).  Selection parity is checked for every (h, i, j).  Outputs are
+compared element by element: every element where the oracle is cheap (C2 at
+both betas; C5 and C5b at beta = 3; one whole head of C3 at beta = 1, with
+sampled blocks of its first and last heads), elsewhere on sampled query
+blocks that the oracle computes one by one, including the first, middle and
+ragged last block of first, middle and last heads.  The dense kernel (the
+speedup baseline) is compared with textbook attention on sampled C3 rows."""
 import math
 
 import numpy as np
 import pytest
 import torch
 
+import oracle
 from block_sparse_attention_23_amd import binding
 from block_sparse_attention_23_amd import inputs as gen
 
-from .parity import block_rows, run_and_check
+from .parity import block_rows, check_output, run_and_check, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -29,6 +33,14 @@ def workload_inputs(name):
 
 CASES = [(n, b) for n in ("C2", "C3", "C4", "C5", "C5b", "C6", "C6b") for b in gen.WORKLOADS[n].betas]
 
+# (workload, beta) -> heads whose every output element is compared
+EVERY_ELEMENT = {("C2", -math.inf): "all", ("C2", 1.0): "all", ("C5", 3.0): "all",
+                 ("C5b", 3.0): "all", ("C3", 1.0): [20]}
+
+
+def sampled_blocks(N):
+    return sorted({0, 1, N // 3, N // 2, N - 2, N - 1})
+
 
 @pytest.mark.parametrize("name,beta", CASES, ids=[f"{n}-beta{b}" for n, b in CASES])
 def test_workload_full_size(name, beta):
@@ -36,11 +48,40 @@ def test_workload_full_size(name, beta):
     w = gen.WORKLOADS[name]
     inp = workload_inputs(name)
     H, N, L, B = w.H, w.N, w.L, w.B
-    heads = sorted({0, H // 2, H - 1})
-    blocks = sorted({0, 1, N // 3, N // 2, N - 2, N - 1})
-    rows = block_rows(L, B, [(h, i) for h in heads for i in blocks])
+    full = EVERY_ELEMENT.get((name, beta))
+    if full == "all":
+        rows = None
+    else:
+        heads = sorted({0, H // 2, H - 1})
+        pairs = [(h, i) for h in heads for i in sampled_blocks(N)]
+        if full:
+            pairs = [(h, i) for h in heads if h not in full for i in sampled_blocks(N)]
+            pairs += [(h, i) for h in full for i in range(N)]
+        rows = block_rows(L, B, pairs)
     s = run_and_check(inp, B, beta, rows=rows)
     print(f"{name} beta={beta}: kept={s['kept_frac']:.4f} flips={s['flips']} "
-          f"max_err={s['max_err']:.3e} mean_err={s['mean_err']:.3e}", flush=True)
+          f"max_err={s['max_err']:.3e} mean_err={s['mean_err']:.3e} over {s['compared']} elements",
+          flush=True)
+    if full == "all":
+        assert s["compared"] == H * L * w.d
     if beta == -math.inf:
         assert s["kept_frac"] == 1.0
+
+
+def test_dense_kernel_c3_sampled_rows():
+    """sol_attn_dense over the whole C3 layer; sampled query blocks of the
+    first, middle and last heads against textbook softmax attention."""
+    w = gen.WORKLOADS["C3"]
+    inp = workload_inputs("C3")
+    q, k, v = to_device(inp)
+    out = binding.attn_dense(q, k, v)
+    torch.cuda.synchronize()
+    heads = sorted({0, w.H // 2, w.H - 1})
+    rows = block_rows(w.L, w.B, [(h, i) for h in heads for i in sampled_blocks(w.N)])
+    ref = oracle.dense(inp.q, inp.k, inp.v, rows=rows)
+    hidx = torch.tensor(rows[:, 0], device=out.device, dtype=torch.long)
+    ridx = torch.tensor(rows[:, 1], device=out.device, dtype=torch.long)
+    got = out[hidx, ridx].float().cpu().numpy()
+    s = check_output(got, ref, "bf16")
+    print(f"C3 dense: max_err={s['max_err']:.3e} mean_err={s['mean_err']:.3e} over {got.size} elements",
+          flush=True)
