@@ -27,6 +27,13 @@ HIPCC_FLAGS = [
 ]
 
 
+def digest_flags(extra=()):
+    """The compiler flags that enter the digest: all but the include paths,
+    which depend on where the tree sits (the same tree is built in one place
+    and loaded from another)."""
+    return [f for f in HIPCC_FLAGS + list(extra) if not f.startswith("-I")]
+
+
 def source_digest(extra=()) -> str:
     """sha256 over the library's sources, headers and compiler flags."""
     import hashlib
@@ -34,7 +41,7 @@ def source_digest(extra=()) -> str:
     for f in SOURCES + HEADERS:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode() + b"\0" + fh.read() + b"\0")
-    h.update(" ".join(HIPCC_FLAGS + list(extra)).encode())
+    h.update(" ".join(digest_flags(extra)).encode())
     return h.hexdigest()
 
 
