@@ -162,6 +162,12 @@ def test_library_built_from_current_sources(lib):
     assert build.built_digest() == build.source_digest()
 
 
+def test_digest_does_not_depend_on_the_tree_location():
+    """The tree is built in one directory and run from another: no path may
+    enter the digest."""
+    assert not any(build.ROOT in f or f.startswith("-I") for f in build.digest_flags())
+
+
 def test_stale_library_is_refused(monkeypatch):
     """A library built from other sources (digest mismatch) is not loaded."""
     monkeypatch.setattr(binding, "_LIB", None)
