@@ -34,6 +34,9 @@ _FUNCS = {
                              + [ctypes.c_float, ctypes.c_float, ctypes.c_uint, ctypes.c_int,
                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                 ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "sol_attn_fwd_noalloc": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4
+                             + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                ctypes.c_void_p]),
     "sol_attn_dense": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4
                        + [ctypes.c_void_p, ctypes.c_void_p]),
     "sol_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -212,6 +215,25 @@ def attn_fwd(q, k, v, B, beta, out=None, kept=None, workspace=None, stream=None,
             return out, kept
         _check("sol_attn_fwd_dbg", lib().sol_attn_fwd_dbg(*args, mask.data_ptr(), tau.data_ptr()))
         return out, kept, mask, tau
+
+
+def attn_fwd_noalloc(q, k, v, B, beta, out=None, kept=None, stream=None):
+    """Sol-Attn forward through sol_attn_fwd_noalloc: the library uses its
+    static per-GPU scratch instead of a workspace (the C call allocates
+    nothing; out and kept are created here when not given).  Returns
+    (out, kept_counts)."""
+    H, L, d = _tokens(q, k, v)
+    N = nblocks(L, B)
+    with _on(stream, q.device):
+        if out is None:
+            out = torch.empty_like(q)
+        if kept is None:
+            kept = torch.empty((H, N), dtype=torch.int32, device=q.device)
+    with torch.cuda.device(q.device):
+        _check("sol_attn_fwd_noalloc", lib().sol_attn_fwd_noalloc(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), H, L, d, B, float(beta), _dtype_code(q),
+            out.data_ptr(), kept.data_ptr(), _stream_ptr(stream, q.device)))
+    return out, kept
 
 
 def attn_fwd_variant(q, k, v, B, beta, keep_frac=0.0, drop_approx=False, topk=False, out=None,

@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "sol.h"
 #include "sol_launch.h"
 
@@ -56,7 +58,9 @@ struct Workspace {
     size_t bytes;
 };
 
-Workspace carve(void* base, int H, int L, int d, int B) {
+// lean: the layout of sol_attn_fwd_noalloc for bf16 inputs, which has no
+// fp32 vsum (only the fp32 sweep reads it; the bf16 sweep reads vsum_bf).
+Workspace carve(void* base, int H, int L, int d, int B, bool lean = false) {
     const size_t N = ((size_t)L + B - 1) / B;
     const size_t pooled = align_up(sizeof(float) * (size_t)H * N * d);
     const size_t pooled_bf = align_up(sizeof(uint16_t) * (size_t)H * N * d);
@@ -69,7 +73,7 @@ Workspace carve(void* base, int H, int L, int d, int B) {
     size_t off = 0;
     w.qbar = reinterpret_cast<float*>(p + off); off += pooled;
     w.kbar = reinterpret_cast<float*>(p + off); off += pooled;
-    w.vsum = reinterpret_cast<float*>(p + off); off += pooled;
+    w.vsum = lean ? nullptr : reinterpret_cast<float*>(p + off); off += lean ? 0 : pooled;
     w.tau = reinterpret_cast<float*>(p + off); off += taub;
     w.queues = reinterpret_cast<int*>(p + off); off += qb;
     w.kbar_bf = reinterpret_cast<uint16_t*>(p + off); off += pooled_bf;
@@ -103,9 +107,9 @@ sol::AttnArgs sweep_args(const void* q, const void* k, const void* v, const floa
     return a;
 }
 
-int forward(const void* q, const void* k, const void* v, int H, int L, int d, int B, float beta,
-            sol_dtype_t dt, void* out, int32_t* kept, void* ws, size_t ws_bytes, void* stream,
-            uint32_t* sel_mask, float* tau_out, float keep_frac = 0.0f, unsigned flags = 0u) {
+int check_forward(const void* q, const void* k, const void* v, int H, int L, int d, int B,
+                  float beta, sol_dtype_t dt, const void* out, const int32_t* kept,
+                  const uint32_t* sel_mask, const float* tau_out, float keep_frac, unsigned flags) {
     int st = check_shape(H, L, d, B);
     if (st != SOL_OK) return st;
     st = check_tensors(q, k, v, out, dt);
@@ -115,10 +119,13 @@ int forward(const void* q, const void* k, const void* v, int H, int L, int d, in
     if ((flags & SOL_TOPK) && !(keep_frac >= 0.0f && keep_frac <= 1.0f)) return SOL_EINVAL;
     if (flags && dt != SOL_BF16) return SOL_EUNSUPPORTED;
     if ((sel_mask && !aligned(sel_mask, 4)) || (tau_out && !aligned(tau_out, 4))) return SOL_EINVAL;
-    if (!ws || !aligned(ws, kAlign)) return SOL_EWORKSPACE;
-    const Workspace w = carve(ws, H, L, d, B);
-    if (ws_bytes < w.bytes) return SOL_EWORKSPACE;
+    return SOL_OK;
+}
 
+// pool -> route -> sweep on the stream, with the workspace regions of w
+int launch_forward(const void* q, const void* k, const void* v, int H, int L, int d, int B,
+                   float beta, sol_dtype_t dt, void* out, int32_t* kept, const Workspace& w,
+                   void* stream, uint32_t* sel_mask, float* tau_out, float keep_frac, unsigned flags) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int N = (L + B - 1) / B;
     const int bf16 = dt == SOL_BF16;
@@ -135,6 +142,7 @@ int forward(const void* q, const void* k, const void* v, int H, int L, int d, in
     const int topk = (flags & SOL_TOPK)
                          ? static_cast<int>(fmin((double)N, fmax(0.0, floor((double)keep_frac * N + 0.5))))
                          : -1;
+    // (the routing kernel also clears the sweep's work counters)
     if (sol::launch_route(w.qbar, w.kbar, H, N, d, c, beta, nullptr, tau, kept, sel, w.queues, s,
                           topk, w.mom) != hipSuccess)
         return SOL_EHIP;
@@ -142,6 +150,62 @@ int forward(const void* q, const void* k, const void* v, int H, int L, int d, in
                                  d, B, out, w.queues, sel);
     a.drop_approx = (flags & SOL_DROP_APPROX) ? 1 : 0;
     if (launch_sweep(a, bf16, d, B, false, s) != hipSuccess) return SOL_EHIP;
+    return SOL_OK;
+}
+
+int forward(const void* q, const void* k, const void* v, int H, int L, int d, int B, float beta,
+            sol_dtype_t dt, void* out, int32_t* kept, void* ws, size_t ws_bytes, void* stream,
+            uint32_t* sel_mask, float* tau_out, float keep_frac = 0.0f, unsigned flags = 0u) {
+    const int st = check_forward(q, k, v, H, L, d, B, beta, dt, out, kept, sel_mask, tau_out,
+                                 keep_frac, flags);
+    if (st != SOL_OK) return st;
+    if (!ws || !aligned(ws, kAlign)) return SOL_EWORKSPACE;
+    const Workspace w = carve(ws, H, L, d, B);
+    if (ws_bytes < w.bytes) return SOL_EWORKSPACE;
+    return launch_forward(q, k, v, H, L, d, B, beta, dt, out, kept, w, stream, sel_mask, tau_out,
+                          keep_frac, flags);
+}
+
+// ---------------------------------------------------------------------------
+// The allocation-free forward pass (sol_attn_fwd_noalloc): its workspace is
+// this static device array, one copy per GPU, which each GPU holds from the
+// library's first use on it until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: the kernels receive the
+// device address that hipGetSymbolAddress returns for the current device,
+// looked up once per device and kept in scratch_addr.  Every call on a GPU
+// shares that GPU's copy; the kernels write every region before reading it
+// (the routing kernel clears the work counters), so nothing is left over
+// from an earlier call.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[SOL_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_addr[kMaxDevices];  // device address of `scratch` per device, once looked up
+
+// The device address of `scratch` on the device of `stream` (the current
+// device for the null stream): looked up with that device current on the
+// first call for the device, then reused.
+int scratch_on(hipStream_t stream, void** addr) {
+    int dev = -1;
+    if (stream) {
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess) return SOL_EHIP;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return SOL_EHIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return SOL_EHIP;
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    if (!scratch_addr[dev]) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return SOL_EHIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return SOL_EHIP;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return SOL_EHIP;
+        if (e != hipSuccess || !p) return SOL_EHIP;
+        scratch_addr[dev] = p;
+    }
+    *addr = scratch_addr[dev];
     return SOL_OK;
 }
 
@@ -279,6 +343,19 @@ int sol_attn_dense(const void* q, const void* k, const void* v, int H, int L, in
     return SOL_OK;
 }
 
+int sol_attn_fwd_noalloc(const void* q, const void* k, const void* v, int H, int L, int d, int B,
+                         float beta, sol_dtype_t dt, void* out, int32_t* kept_counts, void* stream) {
+    int st = check_forward(q, k, v, H, L, d, B, beta, dt, out, kept_counts, nullptr, nullptr, 0.0f, 0u);
+    if (st != SOL_OK) return st;
+    const bool lean = dt == SOL_BF16;
+    if (carve(nullptr, H, L, d, B, lean).bytes > SOL_NOALLOC_SCRATCH_BYTES) return SOL_ESCRATCH;
+    void* base = nullptr;
+    st = scratch_on(static_cast<hipStream_t>(stream), &base);
+    if (st != SOL_OK) return st;
+    return launch_forward(q, k, v, H, L, d, B, beta, dt, out, kept_counts, carve(base, H, L, d, B, lean),
+                          stream, nullptr, nullptr, 0.0f, 0u);
+}
+
 const char* sol_status_string(int status) {
     switch (status) {
         case SOL_OK: return "success";
@@ -286,6 +363,9 @@ const char* sol_status_string(int status) {
         case SOL_EUNSUPPORTED: return "unsupported shape (d must be 64 or 128, B 32, 64 or 128; N <= 8192)";
         case SOL_EWORKSPACE: return "workspace missing, misaligned or smaller than sol_workspace_bytes()";
         case SOL_EHIP: return "HIP kernel launch failed";
+        case SOL_ESCRATCH:
+            return "problem too large for the static scratch of sol_attn_fwd_noalloc "
+                   "(SOL_NOALLOC_SCRATCH_BYTES); use sol_attn_fwd with a workspace";
         default: return "unknown status";
     }
 }

@@ -17,7 +17,8 @@ namespace sol {
 // tokens.  Thread t reads 16-byte vectors at column chunk t % CH of rows
 // t / CH, t / CH + RG, ...; the RG row-group partial sums are added in a
 // fixed order through LDS.  Optionally also writes bf16 copies of kbar and
-// vsum, which the sweep's approximate path feeds to the MFMA.
+// vsum, which the sweep's approximate path feeds to the MFMA (vsum itself
+// may then be left out).
 // ============================================================================
 template <typename T, int D, int BLK>
 __global__ void __launch_bounds__(256) pool_kernel(const T* __restrict__ q, const T* __restrict__ k,
@@ -104,7 +105,7 @@ __global__ void __launch_bounds__(256) pool_kernel(const T* __restrict__ q, cons
             kbar[o] = m;
             if (kbar_bf) kbar_bf[o] = f32_to_bf16_bits(m);
         } else {
-            vsum[o] = s;
+            if (vsum) vsum[o] = s;
             if (vsum_bf) vsum_bf[o] = f32_to_bf16_bits(s);
         }
     }

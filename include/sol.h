@@ -12,7 +12,8 @@
  * Conventions shared by every entry point:
  *  - Token tensors q, k, v, out are DEVICE pointers to [H][L][d] row-major,
  *    contiguous arrays of `dt` elements (bf16 or fp32), 16-byte aligned.
- *    The caller owns all memory; the library allocates nothing.
+ *    The caller owns all memory; the library allocates nothing (apart from
+ *    the static scratch of sol_attn_fwd_noalloc, see there).
  *  - Blocks are B consecutive tokens; N = ceil(L / B); the last block holds
  *    n_last = L - (N-1)*B valid tokens and is masked, never padded.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call is
@@ -43,7 +44,8 @@ typedef enum {
     SOL_EINVAL = -1,        /* null pointer, non-positive size, NaN beta, bad dtype */
     SOL_EUNSUPPORTED = -2,  /* d, B or N outside the supported set */
     SOL_EWORKSPACE = -3,    /* workspace missing or smaller than sol_workspace_bytes */
-    SOL_EHIP = -4           /* a HIP launch or query failed */
+    SOL_EHIP = -4,          /* a HIP launch or query failed */
+    SOL_ESCRATCH = -5       /* sol_attn_fwd_noalloc: the shape needs more than its static scratch */
 } sol_status_t;
 
 /*
@@ -200,6 +202,34 @@ int sol_attn_fwd_variant(const void* q, const void* k, const void* v,
  */
 int sol_attn_dense(const void* q, const void* k, const void* v,
                    int H, int L, int d, sol_dtype_t dt, void* out, void* stream);
+
+/*
+ * sol_attn_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  It allocates nothing: its workspace is
+ * a static device array of SOL_NOALLOC_SCRATCH_BYTES that the library holds
+ * on each GPU it runs on, from its first use there until the process ends.
+ * Results are those of sol_attn_fwd (the same kernels).
+ *
+ * Arguments as sol_attn_fwd; the kernels run on `stream`, whose device's
+ * copy of the scratch they use (the current device for the NULL stream).
+ * Errors: as sol_attn_fwd; SOL_ESCRATCH when the shape needs more scratch
+ * than SOL_NOALLOC_SCRATCH_BYTES, checked on the host before anything is
+ * enqueued.  The scratch holds, each region rounded up to 256 bytes: the
+ * pooled values (bf16 inputs: two fp32 and two bf16 copies of H*N*d values;
+ * fp32 inputs: three fp32 and two bf16), the thresholds (H*N fp32), the
+ * selection bits (H*N*ceil(N/32) uint32) and the key moments
+ * (H*(2d + d*d) fp32).  The Wan-2.1-shaped layer (40 heads, 75,600 tokens,
+ * d = 128, B = 64, bf16) needs 82.5 MB of the 96 MiB.
+ * Calls on one GPU share its scratch: calls that may overlap in time on one
+ * GPU (on different streams, or from different threads) race and give
+ * undefined results; order them on one stream or use sol_attn_fwd with
+ * distinct workspaces.
+ */
+#define SOL_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+int sol_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                         int H, int L, int d, int B, float beta, sol_dtype_t dt,
+                         void* out, int32_t* kept_counts, void* stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* sol_status_string(int status);

@@ -32,8 +32,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "sol_attn_dense", "sol_attn_fwd", "sol_attn_fwd_dbg", "sol_attn_fwd_variant", "sol_pool",
-        "sol_route",
+        "sol_attn_dense", "sol_attn_fwd", "sol_attn_fwd_dbg", "sol_attn_fwd_noalloc",
+        "sol_attn_fwd_variant", "sol_pool", "sol_route",
         "sol_status_string", "sol_sweep", "sol_workspace_bytes"])
 
 
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for st in (0, -1, -2, -3, -4):
+    for st in (0, -1, -2, -3, -4, -5):
         assert binding.status_string(st)
     assert binding.status_string(7) == "unknown status"
 
@@ -154,6 +154,22 @@ def test_variant_rejects_bad_flags_and_fractions(lib):
         if i == 8:
             bad[9] = 2  # the fraction matters for the fixed budget only
         assert lib.sol_attn_fwd_variant(*bad) == want, (i, val)
+
+
+def test_noalloc_rejects_on_the_host(lib):
+    """sol_attn_fwd_noalloc checks its arguments, then the scratch its shape
+    needs against SOL_NOALLOC_SCRATCH_BYTES, before any HIP call."""
+    def call(H=2, L=100, d=64, B=64, beta=1.0, dt=0, q=FAKE, out=FAKE, kept=FAKE):
+        return lib.sol_attn_fwd_noalloc(q, FAKE, FAKE, H, L, d, B, beta, dt, out, kept, None)
+    assert call(q=None) == -1
+    assert call(kept=None) == -1
+    assert call(beta=math.nan) == -1
+    assert call(d=96) == -2
+    assert call(out=FAKE + 2) == -1
+    # 24 heads of 131,072 tokens at d = 128: B = 32 needs about 200 MB (too
+    # much), B = 64 about 90 MB (fits in the 96 MiB)
+    assert call(H=24, L=131072, d=128, B=32) == -5
+    assert "scratch" in binding.status_string(-5)
 
 
 def test_library_built_from_current_sources(lib):
