@@ -53,7 +53,7 @@ def parse():
     return ap.parse_args()
 
 
-SWEEP_SOURCES = ("sol_device.h", "sol_launch.h", "sol_sweep.hip")
+SWEEP_SOURCES = ("sol_device.h", "sol_launch.h", "sol_tile.h", "sol_sweep.hip")
 
 
 def source_digest():

@@ -14,7 +14,7 @@ LIB = os.path.join(PKG, "libsol.so")
 SOURCES = [os.path.join(CSRC, f) for f in
            ("sol_pool_route.hip", "sol_sweep.hip", "sol_f32.hip", "sol_api.hip")]
 HEADERS = [os.path.join(CSRC, "sol_device.h"), os.path.join(CSRC, "sol_launch.h"),
-           os.path.join(INCLUDE, "sol.h")]
+           os.path.join(CSRC, "sol_tile.h"), os.path.join(INCLUDE, "sol.h")]
 ARCH = "gfx950"
 DIGEST = LIB + ".srcdigest"  # digest of the sources and flags LIB was built from
 
