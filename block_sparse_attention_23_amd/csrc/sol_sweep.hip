@@ -88,7 +88,7 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
     const int nwords = (N + 31) / 32;
     const int NG = (N + S::QB - 1) / S::QB;  // 128-row groups per head
     uint32_t* selbits = dyn;                 // [QB][nwords]
-    uint32_t* tiles = dyn + S::QB * nwords;  // up to NC + ceil(N / KPT) entries
+    uint32_t* tiles = dyn + S::QB * nwords;  // up to NC + ceil(N / KPT) (+ 8 at B = 32) entries
     const int myb = (wave * 32) / BLK;       // this wave's query block within the group
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
     const uint32_t dma_base = dma_lane_base<D>(wave_s, lane);
@@ -160,6 +160,7 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             }
             __syncthreads();
             if (wave == 0) {
+                const uint32_t all_blocks = (1u << nqb) - 1u;  // selection masks are 1 .. all_blocks
                 int nt = 0;
                 // approximate chunks that hold an unselected block of a query
                 // block (none when the unselected blocks are dropped)
@@ -200,22 +201,51 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                         nt += __popcll(m);
                     }
                 } else {
-                    // B = 32: union element r goes to entry r / 2, as j1 (r
-                    // even) or j2 (r odd); within the one wave the j1 store
-                    // precedes the j2 read-modify-write of the same entry
-                    int nu = 0;
+                    // B = 32: key blocks that the same query blocks select
+                    // share a 64-key tile, so both halves of a tile serve the
+                    // same waves.  Key blocks are taken in ascending order;
+                    // lane m of `pend` holds a block with selection mask m
+                    // still waiting for a partner (-1: none).  In a chunk of
+                    // 64 blocks, those of mask m pair up in order, the first
+                    // with the pending one; an odd last one waits.  Blocks
+                    // left waiting at the end get a tile of their own.
+                    int pend = -1;
                     for (int j0 = 0; j0 < N; j0 += 64) {
                         const int j = j0 + lane;
-                        bool any = false;
+                        uint32_t part = 0;
                         if (j < N)
-                            for (int b = 0; b < nqb; ++b) any |= ((selbits[b * nwords + (j >> 5)] >> (j & 31)) & 1u) != 0;
-                        const uint64_t m = __ballot(any);
-                        const int r = nu + __popcll(m & ((1ull << lane) - 1ull));
-                        if (any && !(r & 1)) tiles[nt + (r >> 1)] = (uint32_t)j;
-                        if (any && (r & 1)) tiles[nt + (r >> 1)] |= ((uint32_t)j << 13) | (1u << 26);
-                        nu += __popcll(m);
+                            for (int b = 0; b < nqb; ++b)
+                                part |= ((selbits[b * nwords + (j >> 5)] >> (j & 31)) & 1u) << b;
+                        for (uint32_t mk = 1; mk <= all_blocks; ++mk) {
+                            const uint64_t bm = __ballot(part == mk);
+                            if (bm == 0) continue;
+                            const int c = __popcll(bm);
+                            const int r = __popcll(bm & ((1ull << lane) - 1ull));  // rank among mask mk
+                            const int p = __builtin_amdgcn_readlane(pend, (int)mk);
+                            const int q = p >= 0 ? 1 : 0;  // the pending block takes the first one
+                            if (part == mk) {
+                                if (q && r == 0) {
+                                    tiles[nt] = (uint32_t)p | ((uint32_t)j << 13) | (1u << 26);
+                                } else if (((r - q) & 1) == 0 && r + 1 < c) {
+                                    // j1 of a pair whose j2 is the next block of mask mk
+                                    tiles[nt + q + ((r - q) >> 1)] = (uint32_t)j;
+                                }
+                            }
+                            if (part == mk && r >= q && ((r - q) & 1) == 1)
+                                tiles[nt + q + ((r - q) >> 1)] |= ((uint32_t)j << 13) | (1u << 26);
+                            const int rest = c - q;  // blocks after the one the pending block took
+                            nt += q + (rest >> 1);
+                            // the new pending block of mask mk: the last one when rest is odd
+                            const int last = 63 - __builtin_clzll(bm);
+                            const int np = (rest & 1) ? __builtin_amdgcn_readlane(j, last) : -1;
+                            if (lane == (int)mk) pend = np;
+                        }
                     }
-                    nt += (nu + 1) >> 1;
+                    // blocks still waiting: a tile each (no second half)
+                    const uint64_t wb = __ballot(lane >= 1 && lane <= (int)all_blocks && pend >= 0);
+                    if (lane >= 1 && lane <= (int)all_blocks && pend >= 0)
+                        tiles[nt + __popcll(wb & ((1ull << lane) - 1ull))] = (uint32_t)pend;
+                    nt += __popcll(wb);
                 }
                 if (lane == 0) misc_s[1] = nt;
             }
@@ -567,9 +597,10 @@ hipError_t sweep_t(const AttnArgs& a, hipStream_t s) {
     auto kern = sweep_bf16_kernel<D, BLK, DENSE>;
     const int NC = (a.N + S::TB - 1) / S::TB;
     // selection bits of the group's query blocks, then at most NC approximate
-    // and ceil(N / KPT) exact tile-list entries
+    // and ceil(N / KPT) exact tile-list entries (at B = 32 up to 8 more: one
+    // unpaired key block per selection mask)
     const size_t dyn = DENSE ? 0 : sizeof(uint32_t) * ((size_t)S::QB * ((a.N + 31) / 32) + NC +
-                                                       (a.N + S::KPT - 1) / S::KPT);
+                                                       (a.N + S::KPT - 1) / S::KPT + (S::KPT == 2 ? 8 : 0));
     int grid;
     if (DENSE) {
         const int NG = (a.N + S::QB - 1) / S::QB;
