@@ -47,6 +47,10 @@ def parse():
                     help="instead of the benchmark line: error against dense attention and time "
                          "per forward of Sol-Attn, keep-or-drop and a fixed top-k budget at "
                          "equal kept fraction, per beta (one JSON line)")
+    ap.add_argument("--schedule", action="store_true",
+                    help="instead of the benchmark line: the sweep's per-workgroup finish times under "
+                         "the per-XCD locality queues and under a longest-first claim order, per beta "
+                         "(one JSON line)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
@@ -215,6 +219,72 @@ def ablation(args, np, torch, binding, gen):
                       "error": "relative L2 over all outputs", "rows": rows}))
 
 
+def schedule(args, np, torch, binding, gen):
+    """Load balance of the sweep's persistent workgroups ("dynamic but
+    potentially imbalanced budgets"): for each beta, the sweep kernel runs
+    with the per-XCD locality queues (the library's order) and with a
+    longest-first order (group items by their tile count, descending), each
+    recording per item its claim and end times on the GPU's constant clock.
+    Reports the kernel time (HIP events), the spread of workgroup finish
+    times (first to last) and the mean idle time of a workgroup after its
+    last item, in ms."""
+    w = gen.WORKLOADS[args.workload]
+    betas = [float(b) for b in args.betas.split(",")] if args.betas else [min(w.betas), max(w.betas)]
+    if w.dtype != "bf16":
+        raise SystemExit("--schedule measures the bf16 sweep")
+    H, L, d, B, N = w.H, w.L, w.d, w.B, w.N
+    QB = 128 // B
+    G = -(-N // QB)
+    TB = max(B, 64)
+    NC = -(-N // TB)
+    log(f"[schedule] generating {w.name}: {w.desc}")
+    inp = gen.generate(w)
+    q, k, v = [torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+               for b in (inp.q_bits, inp.k_bits, inp.v_bits)]
+    del inp
+    ws = binding.alloc_workspace(H, L, d, B, "cuda")
+    qbar, kbar, vsum = binding.pool(q, k, v, B)
+    bits = torch.empty((H, N, binding.sel_words(N)), dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    rows = []
+    for beta in betas:
+        tau, kept = binding.route(qbar, kbar, L, B, beta, sel_bits=bits, workspace=ws)
+        sel = binding.unpack_mask(bits, N).astype(bool)  # [H][N][N]
+        pad = G * QB - N
+        selg = np.pad(sel, ((0, 0), (0, pad), (0, 0))).reshape(H, G, QB, N)
+        exact = selg.any(axis=2).sum(axis=2)  # union of the group's selections, key blocks
+        exact_tiles = exact * (B // 64) if B >= 64 else (exact + 1) // 2
+        padk = NC * TB - N
+        unsel = ~np.pad(sel, ((0, 0), (0, pad), (0, padk)), constant_values=True).reshape(H, G, QB, NC, TB)
+        approx_tiles = unsel.any(axis=4).any(axis=2).sum(axis=2) * (TB // 64)
+        cost = (exact_tiles + approx_tiles).reshape(-1)
+        lpt = torch.from_numpy(np.argsort(-cost, kind="stable").astype(np.int32)).cuda()
+        res = {"beta": beta, "kept_frac": float(sel.mean()), "items": int(H * G),
+               "tiles_per_item": {"mean": float(cost.mean()), "min": int(cost.min()), "max": int(cost.max())}}
+        for name, order in (("xcd_queues", None), ("longest_first", lpt)):
+            fn = lambda: binding.sweep_timed(q, k, v, qbar, kbar, vsum, tau, B, bits, order=order, out=out,
+                                             workspace=ws)
+            ms, _ = time_loop(fn, args.steps, args.warmup, torch)
+            _, clock = fn()
+            torch.cuda.synchronize()
+            c = clock.cpu().numpy()
+            t0 = c[:, 0].min()
+            ticks = c[:, 1].max() - t0
+            tick_ms = ms / ticks  # the clock's period, from the same launch's HIP-event time
+            wg = c[:, 2]
+            finish = np.array([c[wg == x, 1].max() for x in np.unique(wg)]) - t0
+            end = finish.max()
+            res[name] = {"kernel_ms": ms, "finish_spread_ms": float((end - finish.min()) * tick_ms),
+                         "mean_idle_after_last_item_ms": float((end - finish).mean() * tick_ms),
+                         "mean_item_ms": float(((c[:, 1] - c[:, 0]).mean()) * tick_ms),
+                         "workgroups": int(len(finish)), "clock_mhz": 1e-3 / tick_ms}
+            log(f"[schedule] beta={beta} {name}: {ms:.3f} ms, finish spread "
+                f"{res[name]['finish_spread_ms']:.3f} ms, mean idle at end "
+                f"{res[name]['mean_idle_after_last_item_ms']:.3f} ms")
+        rows.append(res)
+    print(json.dumps({"schedule": w.name, "rows": rows}))
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -233,6 +303,8 @@ def main():
     binding.lib()
     if args.ablation:
         return ablation(args, np, torch, binding, gen)
+    if args.schedule:
+        return schedule(args, np, torch, binding, gen)
     w = gen.WORKLOADS[args.workload]
     betas = ([float(b) for b in args.betas.split(",")] if args.betas else
              [w.headline_beta] + [b for b in w.betas if b != w.headline_beta])

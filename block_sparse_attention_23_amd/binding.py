@@ -23,6 +23,8 @@ _FUNCS = {
                   + [ctypes.c_float] + [ctypes.c_void_p] * 4 + [ctypes.c_size_t, ctypes.c_void_p]),
     "sol_sweep": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 5
                   + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t] + [ctypes.c_void_p] * 3),
+    "sol_sweep_timed": (ctypes.c_int, [ctypes.c_void_p] * 7 + [ctypes.c_int] * 5
+                        + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t] + [ctypes.c_void_p] * 4),
     "sol_attn_fwd": (ctypes.c_int, [ctypes.c_void_p] * 3 + [ctypes.c_int] * 4
                      + [ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
@@ -188,6 +190,37 @@ def sweep(q, k, v, qbar, kbar, vsum, tau, B, out=None, workspace=None, sel_bits=
             None if sel_bits is None else sel_bits.data_ptr(),
             None if sel_mask is None else sel_mask.data_ptr(), _stream_ptr(stream, q.device)))
     return out
+
+
+def group_items(H, N, B):
+    """Work items of the sweep: H heads x ceil(N / (128 / B)) groups of 128 query rows."""
+    return H * -(-N // (128 // B))
+
+
+def sweep_timed(q, k, v, qbar, kbar, vsum, tau, B, sel_bits, order=None, out=None, workspace=None,
+                stream=None):
+    """sol_sweep (bf16) recording, per group item, the claim time, end time
+    (100 MHz clock) and workgroup; `order` (int32 [items]) claims the items in
+    that order instead of from the per-XCD queues.  Returns (out, clock)
+    with clock an int64 [items][3] tensor."""
+    H, L, d = _tokens(q, k, v)
+    n = group_items(H, nblocks(L, B), B)
+    with _on(stream, q.device):
+        if out is None:
+            out = torch.empty_like(q)
+        if workspace is None:
+            workspace = alloc_workspace(H, L, d, B, q.device)
+        clock = torch.zeros((n, 3), dtype=torch.int64, device=q.device)
+    if order is not None and (order.dtype != torch.int32 or order.numel() != n or not order.is_cuda):
+        raise ValueError(f"order must be a device int32 tensor of {n} items")
+    with torch.cuda.device(q.device):
+        _check("sol_sweep_timed", lib().sol_sweep_timed(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), qbar.data_ptr(), kbar.data_ptr(),
+            vsum.data_ptr(), tau.data_ptr(), H, L, d, B, _dtype_code(q), out.data_ptr(),
+            workspace.data_ptr(), workspace.numel(), sel_bits.data_ptr(),
+            None if order is None else order.data_ptr(), clock.data_ptr(),
+            _stream_ptr(stream, q.device)))
+    return out, clock
 
 
 def attn_fwd(q, k, v, B, beta, out=None, kept=None, workspace=None, stream=None, debug=False):

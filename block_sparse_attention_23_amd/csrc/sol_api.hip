@@ -301,6 +301,36 @@ int sol_sweep(const void* q, const void* k, const void* v, const float* qbar, co
     return SOL_OK;
 }
 
+int sol_sweep_timed(const void* q, const void* k, const void* v, const float* qbar, const float* kbar,
+                    const float* vsum, const float* tau, int H, int L, int d, int B, sol_dtype_t dt,
+                    void* out, void* workspace, size_t ws_bytes, const uint32_t* sel_bits,
+                    const int32_t* order, uint64_t* item_clock, void* stream) {
+    int st = check_shape(H, L, d, B);
+    if (st != SOL_OK) return st;
+    st = check_tensors(q, k, v, out, dt);
+    if (st != SOL_OK) return st;
+    if (dt != SOL_BF16) return SOL_EUNSUPPORTED;
+    if (!qbar || !kbar || !vsum || !tau || !sel_bits || !item_clock) return SOL_EINVAL;
+    if (!aligned(qbar, 16) || !aligned(kbar, 16) || !aligned(vsum, 16) || !aligned(tau, 4) ||
+        !aligned(sel_bits, 4) || (order && !aligned(order, 4)) || !aligned(item_clock, 8))
+        return SOL_EINVAL;
+    if (!workspace || !aligned(workspace, kAlign)) return SOL_EWORKSPACE;
+    const Workspace w = carve(workspace, H, L, d, B);
+    if (ws_bytes < w.bytes) return SOL_EWORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int N = (L + B - 1) / B;
+    // bf16 operands of the approximate path; the kernel clears the work counters
+    if (sol::launch_pooled_to_bf16(kbar, vsum, (size_t)H * N * d, w.kbar_bf, w.vsum_bf, w.queues, s) !=
+        hipSuccess)
+        return SOL_EHIP;
+    sol::AttnArgs a = sweep_args(q, k, v, qbar, kbar, vsum, tau, w.kbar_bf, w.vsum_bf, H, L, d, B, out,
+                                 w.queues, sel_bits);
+    a.order = order;
+    a.trace = reinterpret_cast<unsigned long long*>(item_clock);
+    if (launch_sweep(a, 1, d, B, false, s) != hipSuccess) return SOL_EHIP;
+    return SOL_OK;
+}
+
 int sol_attn_fwd(const void* q, const void* k, const void* v, int H, int L, int d, int B, float beta,
                  sol_dtype_t dt, void* out, int32_t* kept_counts, void* workspace, size_t ws_bytes,
                  void* stream) {

@@ -118,4 +118,14 @@ __device__ __forceinline__ int claim_item(int* queues, int H, int N) {
     return -1;
 }
 
+// Claims from a caller-given order instead: one counter (queues[0]) walks
+// order[0 .. total-1].  Returns the item, or -1 once the order is exhausted
+// (or at an entry outside 0 .. total-1, which ends the claiming workgroup).
+__device__ __forceinline__ int claim_ordered(int* queues, const int* order, int total) {
+    const int kk = atomicAdd(&queues[0], 1);
+    if (kk < 0 || kk >= total) return -1;
+    const int it = order[kk];
+    return (it >= 0 && it < total) ? it : -1;
+}
+
 }  // namespace sol

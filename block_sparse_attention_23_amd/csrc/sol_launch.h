@@ -24,6 +24,9 @@ struct AttnArgs {
     float c;             // 1/sqrt(d): proxy-score scale
     float c_log2e;       // 1/sqrt(d) * log2(e): attention logits in base 2
     int drop_approx;     // bf16 sweep: leave the unselected blocks out (keep-or-drop)
+    // bf16 sweep, for scheduling measurements (both null in the forward pass):
+    const int* order;          // [H G] group items in claim order, or null: the per-XCD queues
+    unsigned long long* trace; // [H G][3] per item: claim time, end time (100 MHz clock), workgroup
 };
 
 // Each returns hipSuccess or the launch error.

@@ -130,16 +130,30 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
         dense_item = idx;
     }
 
+    int prev_item = -1;  // (clock records) the item this workgroup finished last
     for (;;) {
         int item;
         if (DENSE) {
             item = dense_item;
         } else {
             __syncthreads();
-            if (tid == 0) misc_s[0] = claim_item(a.queues, H, NG);
+            if (tid == 0) {
+                const int it = a.order ? claim_ordered(a.queues, a.order, H * NG) : claim_item(a.queues, H, NG);
+                if (a.trace) {
+                    // every wave has finished prev_item (the barrier above)
+                    const unsigned long long now = __builtin_amdgcn_s_memrealtime();
+                    if (prev_item >= 0) a.trace[3 * (size_t)prev_item + 1] = now;
+                    if (it >= 0) {
+                        a.trace[3 * (size_t)it] = now;
+                        a.trace[3 * (size_t)it + 2] = blockIdx.x;
+                    }
+                }
+                misc_s[0] = it;
+            }
             __syncthreads();
             item = __builtin_amdgcn_readfirstlane(misc_s[0]);
             if (item < 0) break;
+            prev_item = item;
         }
         const int h = item / NG, gi = item % NG;
         const int i0 = gi * S::QB;

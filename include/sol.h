@@ -126,6 +126,30 @@ int sol_sweep(const void* q, const void* k, const void* v,
               uint32_t* sel_mask, void* stream);
 
 /*
+ * sol_sweep (bf16, with the caller's selection bits) for scheduling
+ * measurements: the same kernel, recording for every group item when a
+ * workgroup claimed it and when it finished, and optionally claiming items
+ * in a caller-given order instead of from the per-XCD queues.  The abstract
+ * notes that selection gives query blocks "dynamic but potentially
+ * imbalanced budgets"; this measures what the claim order does about it.
+ * A group item is one workgroup's 128 query rows of one head: item
+ * h * G + g for g < G = ceil(N / (128 / B)) (B = 64: pairs of query blocks).
+ * order      : DEVICE int32 [H*G], a permutation of 0 .. H*G-1 (claimed in
+ *              that order by one counter), or NULL for the per-XCD queues.
+ *              An entry outside 0 .. H*G-1 ends the claiming workgroup.
+ * item_clock : DEVICE uint64 [H*G][3], written: claim time, end time (the
+ *              100 MHz constant clock of s_memrealtime) and workgroup index.
+ * Other arguments as sol_sweep (sel_bits required).  Outputs are those of
+ * sol_sweep for the same selection (bit for bit with order NULL).
+ * Errors: as sol_sweep; fp32 inputs: SOL_EUNSUPPORTED.
+ */
+int sol_sweep_timed(const void* q, const void* k, const void* v,
+                    const float* qbar, const float* kbar, const float* vsum, const float* tau,
+                    int H, int L, int d, int B, sol_dtype_t dt, void* out,
+                    void* workspace, size_t ws_bytes, const uint32_t* sel_bits,
+                    const int32_t* order, uint64_t* item_clock, void* stream);
+
+/*
  * Sol-Attn forward ("Sol-Attn" visual explainer: Eq. (4) selection rule,
  * Eq. (5) statistics over all N key blocks, Eq. (9) denominator, Eq. (10)
  * numerator, Eq. (11) token-to-pooled-block tile; abstract: one

@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "sol_attn_dense", "sol_attn_fwd", "sol_attn_fwd_dbg", "sol_attn_fwd_noalloc",
         "sol_attn_fwd_variant", "sol_pool", "sol_route",
-        "sol_status_string", "sol_sweep", "sol_workspace_bytes"])
+        "sol_status_string", "sol_sweep", "sol_sweep_timed", "sol_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -119,6 +119,19 @@ def test_stage_entry_points_reject_bad_arguments(lib):
     bad = list(args)
     bad[15] = FAKE + 2  # misaligned selection bits
     assert lib.sol_sweep(*bad) == -1
+
+
+def test_sweep_timed_rejects_bad_arguments(lib):
+    # (q, k, v, qbar, kbar, vsum, tau, H, L, d, B, dt, out, ws, ws_bytes, bits, order, clock, stream)
+    ok = [FAKE] * 7 + [1, 100, 64, 64, 0, FAKE, FAKE_WS, 1 << 30, FAKE, None, FAKE, None]
+    for i, val, want in [(11, 1, -2),       # fp32 inputs: bf16 sweep only
+                         (15, None, -1),    # selection bits required
+                         (17, None, -1),    # clock records required
+                         (16, FAKE + 2, -1),  # misaligned order
+                         (13, None, -3)]:   # workspace
+        bad = list(ok)
+        bad[i] = val
+        assert lib.sol_sweep_timed(*bad) == want, (i, val)
 
 
 def test_binding_refuses_cpu_tensors(lib):

@@ -294,3 +294,29 @@ def test_concurrent_calls_with_distinct_workspaces():
     s2.synchronize()
     assert torch.equal(oa, ref_a[0]) and torch.equal(kpa, ref_a[1])
     assert torch.equal(ob, ref_b[0]) and torch.equal(kpb, ref_b[1])
+
+
+@pytest.mark.parametrize("B", [64, 32, 128])
+def test_sweep_timed_matches_sweep_and_records_every_item(B):
+    """sol_sweep_timed runs the sweep kernel itself: with the per-XCD queues
+    and with a shuffled claim order it reproduces sol_sweep bit for bit (each
+    group item is computed the same way whoever claims it), and it records
+    every item once, with its claim before its end."""
+    inp = grid_inp(3, 3000, 128, "bf16", seed=19)
+    q, k, v = to_device(inp)
+    H, L, d = q.shape
+    N = -(-L // B)
+    qb, kb, vs = binding.pool(q, k, v, B)
+    bits = torch.empty((H, N, binding.sel_words(N)), dtype=torch.int32, device="cuda")
+    tau, _ = binding.route(qb, kb, L, B, 1.0, sel_bits=bits)
+    ref = binding.sweep(q, k, v, qb, kb, vs, tau, B, sel_bits=bits)
+    n = binding.group_items(H, N, B)
+    out0, c0 = binding.sweep_timed(q, k, v, qb, kb, vs, tau, B, bits)
+    order = torch.from_numpy(np.random.default_rng(3).permutation(n).astype(np.int32)).cuda()
+    out1, c1 = binding.sweep_timed(q, k, v, qb, kb, vs, tau, B, bits, order=order)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, ref) and torch.equal(out1, ref)
+    for c in (c0.cpu().numpy(), c1.cpu().numpy()):
+        assert c.shape == (n, 3)
+        assert np.all(c[:, 0] > 0) and np.all(c[:, 1] >= c[:, 0])
+        assert np.all(c[:, 2] >= 0) and np.all(c[:, 2] < 4096)
