@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--oracle-full-run", default=None, help=argparse.SUPPRESS)
     return ap.parse_args()
 
 
@@ -112,14 +113,59 @@ def time_loop(fn, steps, warmup, torch):
 
 
 def cpu_model():
-    """The host CPU's model name from /proc/cpuinfo (None where absent)."""
+    """The host CPU as /proc/cpuinfo describes it: model name, vendor, family,
+    model and stepping of the first processor, and the processor count."""
+    info, count = {}, 0
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" not in line:
+                continue
+            k, v = (x.strip() for x in line.split(":", 1))
+            if k == "processor":
+                count += 1
+            elif count == 1 and k in ("model name", "vendor_id", "cpu family", "model", "stepping"):
+                info[k] = v
     except OSError:
-        pass
-    return None
+        return None
+    info["processors"] = count
+    return info
+
+
+def oracle_full_run(name):
+    """(Child process) the fp64 oracle over a whole workload at its first
+    beta -- pool, route and the merge of every row -- timed by wall clock;
+    the thread count comes from OMP_NUM_THREADS.  Prints one JSON line."""
+    import numpy as np  # noqa: F401
+    import oracle
+    from block_sparse_attention_23_amd import inputs as gen
+    w = gen.WORKLOADS[name]
+    beta = w.headline_beta if w.headline_beta in w.betas else w.betas[-1]
+    inp = gen.generate(w)
+    oracle.lib()
+    t0 = time.perf_counter()
+    oracle.attention(inp.q, inp.k, inp.v, w.B, beta)
+    sec = time.perf_counter() - t0
+    print(json.dumps({"workload": name, "beta": beta, "threads": oracle.num_threads(), "seconds": sec,
+                      "dense_equiv_tflops": w.dense_flops / sec / 1e12}))
+
+
+def oracle_full_runs():
+    """Whole-workload oracle times for C1 and C2, on every host thread and on
+    one, each in a child process (OMP_NUM_THREADS set there)."""
+    import subprocess
+    runs = []
+    for name in ("C1", "C2"):
+        for threads in (None, 1):
+            env = dict(os.environ)
+            if threads:
+                env["OMP_NUM_THREADS"] = str(threads)
+            r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-full-run", name],
+                               capture_output=True, text=True, env=env, timeout=600)
+            if r.returncode != 0:
+                raise RuntimeError(f"oracle run {name} failed: {r.stderr[-2000:]}")
+            runs.append(json.loads(r.stdout.strip().splitlines()[-1]))
+            log(f"[bench] oracle {name} in full: {runs[-1]['seconds']:.2f} s on {runs[-1]['threads']} thread(s)")
+    return runs
 
 
 def cpu_baseline(w, inp, beta, target_s):
@@ -287,6 +333,8 @@ def schedule(args, np, torch, binding, gen):
 
 def main():
     args = parse()
+    if args.oracle_full_run:
+        return oracle_full_run(args.oracle_full_run)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
@@ -397,6 +445,7 @@ def main():
         log("[bench] timing the fp64 CPU oracle on a bounded sample ...")
         cpu = cpu_baseline(w, inp, beta0, args.cpu_seconds)
         log(f"[bench] oracle: {cpu['sample']} ({cpu['cores']} threads)")
+        cpu["full_runs"] = oracle_full_runs()
 
     line = {
         "metric": "dense-equiv attn TFLOPS + MFMA util at L=75.6K,d=128 vs beta; kept-block %",

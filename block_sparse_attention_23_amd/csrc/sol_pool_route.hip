@@ -15,8 +15,9 @@ namespace sol {
 // pool: block means of Q and K, block sums of V (Eq. (5) and Eq. (10)
 // legends).  One workgroup per (head, block), one pass over the block's
 // tokens.  Thread t reads 16-byte vectors at column chunk t % CH of rows
-// t / CH, t / CH + RG, ...; the RG row-group partial sums are added in a
-// fixed order through LDS.  Optionally also writes bf16 copies of kbar and
+// t / CH, t / CH + RG, ...; the row-group partial sums are added in a fixed
+// order: first across the row groups of a wave (lane swaps), then across the
+// four waves through LDS.  Optionally also writes bf16 copies of kbar and
 // vsum, which the sweep's approximate path feeds to the MFMA (vsum itself
 // may then be left out).
 // ============================================================================
@@ -29,16 +30,17 @@ __global__ void __launch_bounds__(256) pool_kernel(const T* __restrict__ q, cons
                                                    u16* __restrict__ kbar_bf,
                                                    u16* __restrict__ vsum_bf) {
     constexpr int VEC = 16 / sizeof(T);
-    constexpr int CH = D / VEC;
-    constexpr int RG = 256 / CH;
+    constexpr int CH = D / VEC;        // 16-byte chunks per row
+    constexpr int RG = 256 / CH;       // row groups
+    constexpr int RGW = 64 / CH;       // row groups per wave
     constexpr int IT = (BLK + RG - 1) / RG;
-    __shared__ float red[3][RG][D + 1];
+    __shared__ float red[3][4][D];     // per wave, its row groups' sums
 
     const int item = blockIdx.x;  // h * N + j
     const int h = item / N, j = item % N;
     const int t0 = j * BLK;
     const int n = min(BLK, L - t0);
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid >> 6;
     const int ch = tid % CH, rg = tid / CH;
 
     float aq[VEC], ak[VEC], av[VEC];
@@ -81,11 +83,30 @@ __global__ void __launch_bounds__(256) pool_kernel(const T* __restrict__ q, cons
             }
         }
     }
+    // the wave's row groups: lanes l, l + CH, l + 2 CH, ... hold the same
+    // columns (CH = 16 at d = 128 bf16: the four lanes l, l^16, l^32, l^48)
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-        red[0][rg][ch * VEC + e] = aq[e];
-        red[1][rg][ch * VEC + e] = ak[e];
-        red[2][rg][ch * VEC + e] = av[e];
+        if constexpr (RGW == 4) {
+            aq[e] = sum4rows(aq[e]);
+            ak[e] = sum4rows(ak[e]);
+            av[e] = sum4rows(av[e]);
+        } else {
+#pragma unroll
+            for (int off = CH; off < 64; off <<= 1) {
+                aq[e] += __shfl_xor(aq[e], off);
+                ak[e] += __shfl_xor(ak[e], off);
+                av[e] += __shfl_xor(av[e], off);
+            }
+        }
+    }
+    if ((tid & 63) < CH) {
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            red[0][wave][ch * VEC + e] = aq[e];
+            red[1][wave][ch * VEC + e] = ak[e];
+            red[2][wave][ch * VEC + e] = av[e];
+        }
     }
     __syncthreads();
     // means by a correctly rounded division: a block of equal tokens pools
@@ -94,9 +115,7 @@ __global__ void __launch_bounds__(256) pool_kernel(const T* __restrict__ q, cons
     const float fn = static_cast<float>(n);
     for (int x = tid; x < 3 * D; x += 256) {
         const int which = x / D, col = x % D;
-        float s = 0.0f;
-#pragma unroll
-        for (int r = 0; r < RG; ++r) s += red[which][r][col];
+        const float s = (red[which][0][col] + red[which][1][col]) + (red[which][2][col] + red[which][3][col]);
         const size_t o = (size_t)item * D + col;
         if (which == 0) {
             qbar[o] = s / fn;
