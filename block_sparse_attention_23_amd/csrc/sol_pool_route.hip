@@ -17,7 +17,8 @@ namespace sol {
 // tokens.  Thread t reads 16-byte vectors at column chunk t % CH of rows
 // t / CH, t / CH + RG, ...; the row-group partial sums are added in a fixed
 // order: first across the row groups of a wave (lane swaps), then across the
-// four waves through LDS.  Optionally also writes bf16 copies of kbar and
+// four waves through LDS.  Every input byte is read once, so the loads are
+// non-temporal (they do not displace cached data).  Optionally also writes bf16 copies of kbar and
 // vsum, which the sweep's approximate path feeds to the MFMA (vsum itself
 // may then be left out).
 // ============================================================================
@@ -55,9 +56,9 @@ __global__ void __launch_bounds__(256) pool_kernel(const T* __restrict__ q, cons
         for (int u = 0; u < 4; ++u) {
             const int r = rg + (it0 + u) * RG;
             if (it0 + u < IT && r < n) {
-                bq[u] = *reinterpret_cast<const u32x4_t*>(q + base + (size_t)r * D);
-                bk[u] = *reinterpret_cast<const u32x4_t*>(k + base + (size_t)r * D);
-                bv[u] = *reinterpret_cast<const u32x4_t*>(v + base + (size_t)r * D);
+                bq[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(q + base + (size_t)r * D));
+                bk[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(k + base + (size_t)r * D));
+                bv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(v + base + (size_t)r * D));
             } else {
                 bq[u] = bk[u] = bv[u] = u32x4_t{0u, 0u, 0u, 0u};
             }
