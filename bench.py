@@ -78,9 +78,10 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
+def measured_traffic(workload, beta):
     """HBM bytes per sweep launch from the committed PMC summary, if it was
-    taken on the current kernel sources (else None)."""
+    taken on the current kernel sources, for this workload and beta (else
+    None)."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     kv = {}
@@ -89,6 +90,11 @@ def measured_traffic():
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     if kv.get("source_digest") != source_digest():
+        return None
+    try:
+        if kv.get("workload") != workload or float(kv.get("beta", "nan")) != beta:
+            return None
+    except ValueError:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -430,7 +436,7 @@ def main():
     kept_token_pair_frac = pair_tokens / (H * float(L) * L)
     achieved = F_alg / (st["sweep"] * 1e-3) / 1e12
     pool_bytes = 3.0 * H * L * d * (2 if w.dtype == "bf16" else 4) + 3.0 * H * N * d * 4
-    traffic = measured_traffic()
+    traffic = measured_traffic(w.name, beta0)
 
     dense = None
     if not args.no_dense:

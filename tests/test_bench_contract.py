@@ -31,3 +31,21 @@ def test_options_parse():
         sys.argv = old
     assert (a.workload, a.betas, a.steps, a.warmup, a.no_dense, a.no_cpu_baseline, a.ablation) == \
         ("C6", "1.25,1.5", 3, 1, True, True, True)
+
+
+def test_traffic_only_for_the_profiled_workload(tmp_path, monkeypatch):
+    """The PMC summary's bytes are reported for its own workload and beta on
+    the sources it was taken on, and for nothing else."""
+    sys.path.insert(0, ROOT)
+    import bench
+    f = tmp_path / "pmc.txt"
+    f.write_text(f"# comment: ignored\nsource_digest: {bench.source_digest()}\nworkload: C3\n"
+                 "beta: 1.0\nhbm_bytes_per_launch: 1.5e+11\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.measured_traffic("C3", 1.0) == 1.5e11
+    assert bench.measured_traffic("C6", 1.0) is None
+    assert bench.measured_traffic("C3", 1.5) is None
+    f.write_text("source_digest: 0123456789abcdef\nworkload: C3\nbeta: 1.0\n"
+                 "hbm_bytes_per_launch: 1.5e+11\n")
+    assert bench.measured_traffic("C3", 1.0) is None
+
