@@ -67,7 +67,7 @@ Workspace carve(void* base, int H, int L, int d, int B, bool lean = false) {
     const size_t taub = align_up(sizeof(float) * (size_t)H * N);
     const size_t qb = align_up(sizeof(int) * 8);
     const size_t selb = align_up(sizeof(uint32_t) * (size_t)H * N * ((N + 31) / 32));
-    const size_t momb = align_up(sizeof(float) * (size_t)H * (2 * (size_t)d + (size_t)d * d));
+    const size_t momb = align_up(sizeof(float) * (size_t)H * ((size_t)d + (size_t)d * d));
     char* p = static_cast<char*>(base);
     Workspace w;
     size_t off = 0;

@@ -361,79 +361,75 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
 }
 
 // ============================================================================
-// key moments (Eq. (5)), centred: per head the mean pooled key and the
-// covariance of the pooled keys about it, from which the proxy row's
-// population mean and variance follow without forming the row:
+// key moments (Eq. (5)): per head the mean pooled key and the covariance of
+// the pooled keys about it, from which the proxy row's population mean and
+// variance follow without forming the row:
 //     mbar = (1/N) sum_j kbar_j,   Cov = (1/N) sum_j (kbar_j - mbar)(kbar_j - mbar)^T
 //     mu_i = c qbar_i . mbar,      sigma_i^2 = c^2 qbar_i Cov qbar_i^T.
 // This is Eq. (5)'s moment form with the mean taken out before the products
 // are summed (its C minus mbar mbar^T), so sigma_i^2 is a sum of
 // non-negative terms and no large, nearly equal numbers are subtracted when
-// the keys share a large common component.  To keep the centring itself
-// exact in fp32 for keys that are all equal, the keys are first shifted by
-// the head's first pooled key: y_j = kbar_j - kbar_0 (exactly 0 for a key
-// equal to kbar_0), ybar = (1/N) sum_j y_j, and Cov is summed from
-// y_j - ybar; then mbar = kbar_0 + ybar.
+// the keys share a large common component.  The mean, the centring and both
+// sums run in fp64 (the fp32 rounding of the covariance sums would otherwise
+// dominate the error of tau); each centred value is rounded to fp32 once for
+// the on-chip buffer (its product in fp64 is exact), and the results are
+// stored as fp32.  Keys that are all equal give Cov = 0
+// exactly: N <= 8192 copies of one fp32 value sum exactly in fp64, so their
+// mean is that value.
 // Workgroup (h, bi, bj) forms the 32x32 block (bi, bj) of Cov: a first pass
-// takes ybar for its 64 columns (every workgroup sums a column in the same
+// takes the mean of its 64 columns (every workgroup sums a column in the same
 // order, so all of them agree), a second the centred products.  Per head:
-// kbar_0 (D floats), ybar (D), then Cov row-major (D*D).
+// mbar (D floats), then Cov row-major (D*D).
 // ============================================================================
 template <int D>
 __global__ void __launch_bounds__(256) key_moments_kernel(const float* __restrict__ kbar, int N,
                                                           float* __restrict__ mom) {
     constexpr int NBK = D / 32;
-    __shared__ float ka[64][33];
+    __shared__ float ka[64][33];    // centred keys (centred in fp64, rounded once)
     __shared__ float kb[64][33];
-    __shared__ float k0[64];      // kbar_0 at columns 32 bi + e (e < 32), 32 bj + e - 32
-    __shared__ float part[4][64];  // partial column sums of y
-    __shared__ float ym[64];      // ybar at the same columns
+    __shared__ double part[4][64];  // partial column sums
+    __shared__ double mean[64];     // mbar at columns 32 bi + e (e < 32), 32 bj + e - 32
     const int h = blockIdx.x / (NBK * NBK);
     const int bi = (blockIdx.x / NBK) % NBK, bj = blockIdx.x % NBK;
     const int tid = threadIdx.x, a = tid >> 3, b4 = (tid & 7) * 4;
     const float* kh = kbar + (size_t)h * N * D;
     auto col_of = [&](int e) { return e < 32 ? 32 * bi + e : 32 * bj + e - 32; };
-    if (tid < 64) k0[tid] = kh[col_of(tid)];
-    __syncthreads();
 
-    // pass 1: ybar.  Thread (p, e) sums rows j = p, p + 4, ... of column e.
+    // pass 1: mbar.  Thread (p, e) sums rows j = p, p + 4, ... of column e.
     {
         const int e = tid & 63, p = tid >> 6;
         const int col = col_of(e);
-        const float base = k0[e];
-        float s = 0.0f;
-        for (int j = p; j < N; j += 4) s += kh[(size_t)j * D + col] - base;
+        double s = 0.0;
+        for (int j = p; j < N; j += 4) s += static_cast<double>(kh[(size_t)j * D + col]);
         part[p][e] = s;
     }
     __syncthreads();
-    if (tid < 64) ym[tid] = ((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid])) / static_cast<float>(N);
+    if (tid < 64) mean[tid] = ((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid])) / static_cast<double>(N);
     __syncthreads();
 
     // pass 2: Cov block (bi, bj) from the centred keys
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
     for (int j0 = 0; j0 < N; j0 += 64) {
         __syncthreads();
         for (int x = tid; x < 64 * 32; x += 256) {
             const int jj = x >> 5, e = x & 31, j = j0 + jj;
-            ka[jj][e] = j < N ? (kh[(size_t)j * D + 32 * bi + e] - k0[e]) - ym[e] : 0.0f;
-            kb[jj][e] = j < N ? (kh[(size_t)j * D + 32 * bj + e] - k0[32 + e]) - ym[32 + e] : 0.0f;
+            ka[jj][e] = j < N ? static_cast<float>(static_cast<double>(kh[(size_t)j * D + 32 * bi + e]) - mean[e]) : 0.0f;
+            kb[jj][e] = j < N ? static_cast<float>(static_cast<double>(kh[(size_t)j * D + 32 * bj + e]) - mean[32 + e]) : 0.0f;
         }
         __syncthreads();
 #pragma unroll 8
         for (int jj = 0; jj < 64; ++jj) {
-            const float x = ka[jj][a];
+            const double x = ka[jj][a];
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) acc[cc] = __builtin_fmaf(x, kb[jj][b4 + cc], acc[cc]);
+            for (int cc = 0; cc < 4; ++cc) acc[cc] = __builtin_fma(x, static_cast<double>(kb[jj][b4 + cc]), acc[cc]);
         }
     }
-    const float inv = 1.0f / static_cast<float>(N);
-    float* mh = mom + (size_t)h * (2 * D + D * D);
+    const double n = static_cast<double>(N);
+    float* mh = mom + (size_t)h * (D + D * D);
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) mh[2 * D + (32 * bi + a) * D + 32 * bj + b4 + cc] = acc[cc] * inv;
-    if (bj == 0 && tid < 32) {
-        mh[32 * bi + tid] = k0[tid];
-        mh[D + 32 * bi + tid] = ym[tid];
-    }
+    for (int cc = 0; cc < 4; ++cc)
+        mh[D + (32 * bi + a) * D + 32 * bj + b4 + cc] = static_cast<float>(acc[cc] / n);
+    if (bj == 0 && tid < 32) mh[32 * bi + tid] = static_cast<float>(mean[tid]);
 }
 
 // ============================================================================
@@ -470,10 +466,10 @@ __global__ void __launch_bounds__(256) route_moments_kernel(
 
     // thresholds: wave w takes rows 4w .. 4w+3, lane l the columns l + 64 m of
     // v = qbar_r Cov, then e_r = v . qbar_r (= sigma_r^2 / c^2) and
-    // qbar_r . mbar = qbar_r . kbar_0 + qbar_r . ybar by butterflies.
-    // sigma_r = 0 (the pooled keys all equal, or qbar_r orthogonal to their
-    // spread: every s_rj is then mu_r in exact arithmetic) selects no block:
-    // none is strictly above tau_r = mu_r.
+    // qbar_r . mbar by butterflies, all in fp64; tau_r is rounded to fp32
+    // once.  sigma_r = 0 (the pooled keys all equal, or qbar_r orthogonal to
+    // their spread: every s_rj is then mu_r in exact arithmetic) selects no
+    // block: none is strictly above tau_r = mu_r.
     if (tau_in || isinf(beta)) {
         if (tid < R) {
             tau_s[tid] = tau_in ? tau_in[(size_t)h * N + min(i0 + tid, N - 1)] : beta;
@@ -481,47 +477,47 @@ __global__ void __launch_bounds__(256) route_moments_kernel(
         }
     } else {
         constexpr int CPL = D / 64;
-        const float* mh = mom + (size_t)h * (2 * D + D * D);
-        const float* cov = mh + 2 * D;
-        float v[4][CPL];
+        const double c64 = 1.0 / __builtin_sqrt(static_cast<double>(D));
+        const float* mh = mom + (size_t)h * (D + D * D);
+        const float* cov = mh + D;
+        double v[4][CPL];
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
-            for (int m = 0; m < CPL; ++m) v[rr][m] = 0.0f;
+            for (int m = 0; m < CPL; ++m) v[rr][m] = 0.0;
 #pragma unroll 4
         for (int dp = 0; dp < D; ++dp) {
-            float crow[CPL];
+            double crow[CPL];
 #pragma unroll
-            for (int m = 0; m < CPL; ++m) crow[m] = cov[dp * D + lane + 64 * m];
+            for (int m = 0; m < CPL; ++m) crow[m] = static_cast<double>(cov[dp * D + lane + 64 * m]);
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const float qd = qs[4 * wave + rr][dp];
+                const double qd = static_cast<double>(qs[4 * wave + rr][dp]);
 #pragma unroll
-                for (int m = 0; m < CPL; ++m) v[rr][m] = __builtin_fmaf(qd, crow[m], v[rr][m]);
+                for (int m = 0; m < CPL; ++m) v[rr][m] = __builtin_fma(qd, crow[m], v[rr][m]);
             }
         }
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const int r = 4 * wave + rr;
-            float e = 0.0f, mu0 = 0.0f, mu1 = 0.0f;
+            double e = 0.0, mu = 0.0;
 #pragma unroll
             for (int m = 0; m < CPL; ++m) {
                 const int col = lane + 64 * m;
-                e = __builtin_fmaf(qs[r][col], v[rr][m], e);
-                mu0 = __builtin_fmaf(qs[r][col], mh[col], mu0);
-                mu1 = __builtin_fmaf(qs[r][col], mh[D + col], mu1);
+                const double qc = static_cast<double>(qs[r][col]);
+                e = __builtin_fma(qc, v[rr][m], e);
+                mu = __builtin_fma(qc, static_cast<double>(mh[col]), mu);
             }
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) {
                 e += __shfl_xor(e, off);
-                mu0 += __shfl_xor(mu0, off);
-                mu1 += __shfl_xor(mu1, off);
+                mu += __shfl_xor(mu, off);
             }
             if (lane == 0) {
-                const float m_ = c * (mu0 + mu1);
-                const float var = c * c * fmaxf(e, 0.0f);
-                tau_s[r] = var > 0.0f ? __builtin_fmaf(beta, sqrtf(var), m_) : m_;
-                tau_cmp[r] = var > 0.0f ? tau_s[r] : INFINITY;
+                const double m_ = c64 * mu;
+                const double var = c64 * c64 * fmax(e, 0.0);
+                tau_s[r] = static_cast<float>(var > 0.0 ? __builtin_fma(static_cast<double>(beta), __builtin_sqrt(var), m_) : m_);
+                tau_cmp[r] = var > 0.0 ? tau_s[r] : INFINITY;
             }
         }
     }

@@ -54,7 +54,7 @@ typedef enum {
  * per-query-block thresholds (H*N fp32), the scheduler's queue counters, bf16
  * copies of the pooled keys and summed values (2 x H*N*d bf16), the
  * selection bits (H*N*ceil(N/32) uint32) and the key moments
- * (H*(2d + d*d) fp32).  0 for invalid shapes.
+ * (H*(d + d*d) fp32).  0 for invalid shapes.
  */
 size_t sol_workspace_bytes(int H, int L, int d, int B);
 
@@ -91,8 +91,9 @@ int sol_pool(const void* q, const void* k, const void* v,
  * moments of Eq. (5), taken about the mean pooled key (equal in exact
  * arithmetic): mu_i = c qbar_i . mbar and sigma_i^2 = c^2 qbar_i Cov qbar_i^T
  * with mbar = (1/N) sum_j kbar_j and Cov = (1/N) sum_j (kbar_j - mbar)
- * (kbar_j - mbar)^T (computed into the workspace; no subtraction of nearly
- * equal terms when the keys share a large common component).  A row whose
+ * (kbar_j - mbar)^T (summed in fp64 into the workspace as fp32; no
+ * subtraction of nearly equal terms when the keys share a large common
+ * component; mu_i, sigma_i and tau_i in fp64, tau_i rounded to fp32).  A row whose
  * sigma_i is 0 (all its scores equal) keeps no block: none is strictly above
  * tau_i = mu_i.
  * The counts and bits are those the forward pass uses (the same kernels
@@ -243,7 +244,7 @@ int sol_attn_dense(const void* q, const void* k, const void* v,
  * pooled values (bf16 inputs: two fp32 and two bf16 copies of H*N*d values;
  * fp32 inputs: three fp32 and two bf16), the thresholds (H*N fp32), the
  * selection bits (H*N*ceil(N/32) uint32) and the key moments
- * (H*(2d + d*d) fp32).  The Wan-2.1-shaped layer (40 heads, 75,600 tokens,
+ * (H*(d + d*d) fp32).  The Wan-2.1-shaped layer (40 heads, 75,600 tokens,
  * d = 128, B = 64, bf16) needs 82.5 MB of the 96 MiB.
  * Calls on one GPU share its scratch: calls that may overlap in time on one
  * GPU (on different streams, or from different threads) race and give

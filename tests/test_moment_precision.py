@@ -1,16 +1,17 @@
-"""Precision of the Eq. (5) moment route in fp32 ("Sol-Attn" visual explainer,
+"""Precision of the Eq. (5) moment route ("Sol-Attn" visual explainer,
 Eq. (5): the proxy row's mean and variance from the mean pooled key and the
 key second moments), which the routing kernel uses for rows longer than its
-on-chip buffer.  The kernel's arithmetic is emulated on the CPU in numpy
-float32, in its summation order, and its thresholds tau_i = mu_i + beta
-sigma_i are compared with the oracle's fp64 two-pass thresholds.
+on-chip buffer.  The kernel's arithmetic is emulated on the CPU in numpy,
+and its thresholds tau_i = mu_i + beta sigma_i are compared with the oracle's
+fp64 two-pass thresholds.
 
-The centred form (covariance about the mean pooled key, after shifting by the
-first key) stays within 1e-4 even when every key carries a large common
-component (|mu|/sigma ~ 100), while the raw form
-sigma^2 = c^2 qbar C qbar^T - mu^2 loses several 1e-3 there to cancellation:
-more than the 1e-3 band within which a selection may differ from the
-oracle's."""
+The kernel's form (mean and covariance about the mean summed in fp64 and
+stored as fp32; mu, sigma and tau in fp64, tau rounded to fp32 once) stays
+within a few fp32 ulps of the oracle's tau even when every key carries a
+large common component (|mu|/sigma ~ 100), while Eq. (5) as printed in fp32,
+sigma^2 = c^2 qbar C qbar^T - mu^2, loses several 1e-3 there to
+cancellation: more than the 1e-3 band within which a selection may differ
+from the oracle's."""
 import numpy as np
 import pytest
 
@@ -46,28 +47,25 @@ def tau_raw_form(qbar, kbar, beta):
     return (mu + F32(beta) * np.sqrt(var)).astype(F32)
 
 
-def tau_centred_form(qbar, kbar, beta):
-    """The kernel's form in float32: y_j = kbar_j - kbar_0, ybar from four
-    partial sums (j mod 4), Cov = (1/N) sum (y_j - ybar)(y_j - ybar)^T,
-    mu = c qbar . (kbar_0 + ybar), sigma^2 = c^2 qbar Cov qbar^T; sigma = 0
-    reports tau = mu."""
+def tau_kernel_form(qbar, kbar, beta):
+    """The kernel's form: mbar from four fp64 partial sums (j mod 4),
+    Cov = (1/N) sum_j (kbar_j - mbar)(kbar_j - mbar)^T in fp64 over centred
+    values rounded to fp32, mbar and Cov stored as fp32; then in fp64 mu = c qbar . mbar and sigma^2 = c^2 qbar Cov
+    qbar^T, with c = 1/sqrt(d); tau rounded to fp32; sigma = 0 reports
+    tau = mu."""
     N, d = kbar.shape
-    c = F32(1.0 / np.sqrt(d))
-    k = kbar.astype(F32)
-    k0 = k[0].copy()
-    y = (k - k0).astype(F32)
-    parts = [np.zeros(d, F32) for _ in range(4)]
-    for j in range(N):
-        parts[j % 4] = (parts[j % 4] + y[j]).astype(F32)
-    ym = (((parts[0] + parts[1]).astype(F32) + (parts[2] + parts[3]).astype(F32)).astype(F32)
-          / F32(N)).astype(F32)
-    z = (y - ym).astype(F32)
-    Cov = (_seq_outer_sum(z) * (F32(1.0) / F32(N))).astype(F32)
-    q = qbar.astype(F32)
-    e = np.einsum("ia,ab,ib->i", q, Cov, q).astype(F32)
-    mu = (c * ((q @ k0).astype(F32) + (q @ ym).astype(F32))).astype(F32)
-    var = (c * c * np.maximum(e, F32(0))).astype(F32)
-    return np.where(var > 0, mu + F32(beta) * np.sqrt(var), mu).astype(F32)
+    c = 1.0 / np.sqrt(d)
+    k = kbar.astype(F32).astype(np.float64)
+    parts = [k[p::4].sum(axis=0) for p in range(4)]
+    mean = ((parts[0] + parts[1]) + (parts[2] + parts[3])) / N
+    z = (k - mean).astype(F32).astype(np.float64)  # centred in fp64, rounded once
+    cov = ((z.T @ z) / N).astype(F32).astype(np.float64)
+    m32 = mean.astype(F32).astype(np.float64)
+    q = qbar.astype(F32).astype(np.float64)
+    e = np.einsum("ia,ab,ib->i", q, cov, q)
+    mu = c * (q @ m32)
+    var = c * c * np.maximum(e, 0.0)
+    return np.where(var > 0, mu + beta * np.sqrt(var), mu).astype(F32)
 
 
 @pytest.fixture(scope="module")
@@ -83,15 +81,18 @@ def _shift(d, seed=5):
 
 @pytest.mark.parametrize("a,b,min_ratio", [(0.0, 0.0, 0.0), (20.0, 3.0, 15.0), (60.0, 4.0, 80.0),
                                            (80.0, 5.0, 120.0)])
-def test_centred_moments_keep_tau_within_band(base, a, b, min_ratio):
+def test_kernel_moments_keep_tau_within_band(base, a, b, min_ratio):
     u = _shift(128)
     inp = gen.shifted_inputs(base, q_shift=b * u, k_shift=a * u)
     qbar, kbar, _ = oracle.pool(inp.q, inp.k, inp.v, 64)
     r = oracle.route(qbar, kbar, 1.0)
     ratio = np.median(np.abs(r["mu"][0]) / r["sigma"][0])
     assert ratio >= min_ratio
-    err_c = np.abs(tau_centred_form(qbar[0], kbar[0], 1.0) - r["tau"][0]).max()
-    assert err_c < 1e-4, (ratio, err_c)
+    tau = r["tau"][0]
+    err = np.abs(tau_kernel_form(qbar[0], kbar[0], 1.0) - tau)
+    # within 4 ulps of tau (fp32: 2^-23 relative), and far inside the band
+    assert np.all(err <= 4 * 2.0 ** -23 * np.maximum(np.abs(tau), 1e-3)), (ratio, err.max())
+    assert err.max() < 1e-4
     if ratio > 80:
         # the raw form fails here: this test would catch a return to it
         err_r = np.abs(tau_raw_form(qbar[0], kbar[0], 1.0) - r["tau"][0]).max()
@@ -100,13 +101,13 @@ def test_centred_moments_keep_tau_within_band(base, a, b, min_ratio):
 
 def test_equal_keys_give_zero_spread_exactly(base):
     """Every key token equal: every pooled key equals it exactly (block means
-    by a correctly rounded division), the shifted keys are exactly zero and
-    the centred spread is exactly 0, so the route keeps no block."""
+    by a correctly rounded division), their fp64 mean is that key exactly,
+    the covariance is exactly 0, so tau = mu and the route keeps no block."""
     kc = base.k[0, 0]
     inp = gen.shifted_inputs(base, k_const=kc)
     qbar, kbar, _ = oracle.pool(inp.q, inp.k, inp.v, 64)
     assert np.all(kbar == kbar[0, 0])
-    tau = tau_centred_form(qbar[0], kbar[0], 1.0)
-    q = qbar[0].astype(F32)
-    mu = (F32(1.0 / np.sqrt(128)) * (q @ kbar[0, 0].astype(F32))).astype(F32)
+    tau = tau_kernel_form(qbar[0], kbar[0], 1.0)
+    q = qbar[0].astype(F32).astype(np.float64)
+    mu = ((1.0 / np.sqrt(128)) * (q @ kbar[0, 0].astype(F32).astype(np.float64))).astype(F32)
     assert np.array_equal(tau, mu)
