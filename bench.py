@@ -25,6 +25,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector ALU (the fp32 path computes on the VALU)
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_c3_beta1_pmc.txt")
 
@@ -437,13 +438,15 @@ def main():
     achieved = F_alg / (st["sweep"] * 1e-3) / 1e12
     pool_bytes = 3.0 * H * L * d * (2 if w.dtype == "bf16" else 4) + 3.0 * H * N * d * 4
     traffic = measured_traffic(w.name, beta0)
+    # bf16 tiles run on the bf16 MFMA; the fp32 path on the fp32 vector ALU
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_VALU_TFLOPS
 
     dense = None
     if not args.no_dense:
         fn = lambda: binding.attn_dense(q, k, v, out=out)
         dms, _ = time_loop(fn, max(2, args.steps // 2), 1, torch)
         dt = F_dense / (dms * 1e-3) / 1e12
-        dense = {"ms": dms, "tflops": dt, "mfma_util": dt / PEAK_BF16_TFLOPS}
+        dense = {"ms": dms, "tflops": dt, "mfma_util": dt / peak}
         log(f"[bench] dense: {dms:.3f} ms, {dt:.1f} TFLOP/s")
 
     cpu = None
@@ -470,9 +473,9 @@ def main():
                    "N": N, "beta": head["beta"], "seed": w.seed},
         "kept_block_frac": head["kept_frac"],
         "kept_token_pair_frac": kept_token_pair_frac,
-        "exact_tile_mfma_util": head["F_exact"] / (st["sweep"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+        "exact_tile_mfma_util": head["F_exact"] / (st["sweep"] * 1e-3) / 1e12 / peak,
+        "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": traffic, "kernel": (f"sweep_bf16_kernel<{d}, {B}, false>" if w.dtype == "bf16"
                                                     else f"attn_f32_kernel<{d}, {B}, false>"),
                      "algorithmic_flop_per_launch": F_alg},
@@ -481,11 +484,11 @@ def main():
         "dense_baseline": dense,
         "speedup_vs_dense": (dense["ms"] / head["ms"]) if dense else None,
         # per beta: exact-tile flops over the whole forward's time (pool and
-        # route included) as a fraction of the bf16 peak, and the speedup
+        # route included) as a fraction of the path's peak, and the speedup
         "beta_sweep": [{"beta": r["beta"], "ms": r["ms"], "kept_frac": r["kept_frac"],
                         "tflops_dense_eq": r["tflops_dense_eq"],
                         "exact_tflop": r["F_exact"] / 1e12,
-                        "exact_util_of_forward": r["F_exact"] / (r["ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                        "exact_util_of_forward": r["F_exact"] / (r["ms"] * 1e-3) / 1e12 / peak,
                         "speedup_vs_dense": (dense["ms"] / r["ms"]) if dense else None}
                        for r in results],
         "cpu_baseline": cpu,
