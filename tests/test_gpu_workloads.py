@@ -2,8 +2,9 @@
 configuration the benchmark times (every head and query block runs on the
 GPU).  Selection parity is checked for every (h, i, j).  Outputs are
 compared element by element: every element where the oracle is cheap (C2 at
-both betas; C5 and C5b at beta = 3; one whole head of C3 at beta = 1, with
-sampled blocks of its first and last heads), elsewhere on sampled query
+both betas; C5 and C5b at beta = 3; one whole head of C3 at beta = 1, of C4
+at beta = 1 and of C6 and C6b at beta = 1.25, each with sampled blocks of the
+first, middle and last heads), elsewhere on sampled query
 blocks that the oracle computes one by one, including the first, middle and
 ragged last block of first, middle and last heads.  The dense kernel (the
 speedup baseline) is compared with textbook attention on sampled C3 rows."""
@@ -35,7 +36,8 @@ CASES = [(n, b) for n in ("C2", "C3", "C4", "C5", "C5b", "C6", "C6b") for b in g
 
 # (workload, beta) -> heads whose every output element is compared
 EVERY_ELEMENT = {("C2", -math.inf): "all", ("C2", 1.0): "all", ("C5", 3.0): "all",
-                 ("C5b", 3.0): "all", ("C3", 1.0): [20]}
+                 ("C5b", 3.0): "all", ("C3", 1.0): [20], ("C4", 1.0): [11], ("C6", 1.25): [7],
+                 ("C6b", 1.25): [17]}
 
 
 def sampled_blocks(N):
@@ -64,6 +66,8 @@ def test_workload_full_size(name, beta):
           flush=True)
     if full == "all":
         assert s["compared"] == H * L * w.d
+    elif full:
+        assert s["compared"] >= len(full) * L * w.d
     if beta == -math.inf:
         assert s["kept_frac"] == 1.0
 
