@@ -11,6 +11,8 @@
 
 namespace sol {
 
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+
 // ============================================================================
 // pool: block means of Q and K, block sums of V (Eq. (5) and Eq. (10)
 // legends).  One workgroup per (head, block), one pass over the block's
@@ -378,8 +380,8 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
 // mean is that value.
 // Workgroup (h, bi, bj) forms the 32x32 block (bi, bj) of Cov: a first pass
 // takes the mean of its 64 columns (every workgroup sums a column in the same
-// order, so all of them agree), a second the centred products.  Per head:
-// mbar (D floats), then Cov row-major (D*D).
+// order, so all of them agree), a second the centred products on the fp64
+// matrix instructions.  Per head: mbar (D floats), then Cov row-major (D*D).
 // ============================================================================
 template <int D>
 __global__ void __launch_bounds__(256) key_moments_kernel(const float* __restrict__ kbar, int N,
@@ -391,7 +393,7 @@ __global__ void __launch_bounds__(256) key_moments_kernel(const float* __restric
     __shared__ double mean[64];     // mbar at columns 32 bi + e (e < 32), 32 bj + e - 32
     const int h = blockIdx.x / (NBK * NBK);
     const int bi = (blockIdx.x / NBK) % NBK, bj = blockIdx.x % NBK;
-    const int tid = threadIdx.x, a = tid >> 3, b4 = (tid & 7) * 4;
+    const int tid = threadIdx.x;
     const float* kh = kbar + (size_t)h * N * D;
     auto col_of = [&](int e) { return e < 32 ? 32 * bi + e : 32 * bj + e - 32; };
 
@@ -407,8 +409,13 @@ __global__ void __launch_bounds__(256) key_moments_kernel(const float* __restric
     if (tid < 64) mean[tid] = ((part[0][tid] + part[1][tid]) + (part[2][tid] + part[3][tid])) / static_cast<double>(N);
     __syncthreads();
 
-    // pass 2: Cov block (bi, bj) from the centred keys
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    // pass 2: Cov block (bi, bj) from the centred keys.  Wave w forms the
+    // 16 x 16 quarter (rows 16 (w >> 1), columns 16 (w & 1) of the block) with
+    // fp64 matrix instructions, four key rows per instruction: A[i][k] is
+    // column 16 (w >> 1) + i of row k, B[k][j] column 16 (w & 1) + j of row k.
+    const int wave = tid >> 6, lane = tid & 63;
+    const int ti = wave >> 1, tj = wave & 1;
+    f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
     for (int j0 = 0; j0 < N; j0 += 64) {
         __syncthreads();
         for (int x = tid; x < 64 * 32; x += 256) {
@@ -417,18 +424,21 @@ __global__ void __launch_bounds__(256) key_moments_kernel(const float* __restric
             kb[jj][e] = j < N ? static_cast<float>(static_cast<double>(kh[(size_t)j * D + 32 * bj + e]) - mean[32 + e]) : 0.0f;
         }
         __syncthreads();
-#pragma unroll 8
-        for (int jj = 0; jj < 64; ++jj) {
-            const double x = ka[jj][a];
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) acc[cc] = __builtin_fma(x, static_cast<double>(kb[jj][b4 + cc]), acc[cc]);
+        for (int k0 = 0; k0 < 64; k0 += 4) {
+            const double av = static_cast<double>(ka[k0 + (lane >> 4)][16 * ti + (lane & 15)]);
+            const double bv = static_cast<double>(kb[k0 + (lane >> 4)][16 * tj + (lane & 15)]);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
         }
     }
     const double n = static_cast<double>(N);
     float* mh = mom + (size_t)h * (D + D * D);
+    // element r of lane l is row 4 r + (l >> 4) of column l & 15 (the fp64
+    // instruction's result layout, measured)
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
-        mh[D + (32 * bi + a) * D + 32 * bj + b4 + cc] = static_cast<float>(acc[cc] / n);
+    for (int r = 0; r < 4; ++r)
+        mh[D + (32 * bi + 16 * ti + 4 * r + (lane >> 4)) * D + 32 * bj + 16 * tj + (lane & 15)] =
+            static_cast<float>(acc[r] / n);
     if (bj == 0 && tid < 32) mh[32 * bi + tid] = static_cast<float>(mean[tid]);
 }
 
@@ -438,16 +448,17 @@ __global__ void __launch_bounds__(256) key_moments_kernel(const float* __restric
 // and sigma_i from the moments (Eq. (5), above), then one pass that forms
 // every s_ij (Eq. (11) right-hand side) exactly as the row-holding route
 // does and keeps only the decision s_ij > tau_i, as bits, and their count.
-// One workgroup serves 16 query blocks (one MFMA row tile).  With tau_in,
+// One workgroup serves 16 RT query blocks (RT MFMA row tiles, each pooled-key
+// tile loaded once for all of them).  With tau_in,
 // or beta = +-inf, the thresholds need no moments.
 // ============================================================================
-template <int D>
+template <int D, int RT>
 __global__ void __launch_bounds__(256) route_moments_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, const float* __restrict__ mom,
     int N, int groups_per_head, float c, float beta, const float* __restrict__ tau_in,
     float* __restrict__ tau_out, int32_t* __restrict__ kept, uint32_t* __restrict__ sel, int W,
     int* __restrict__ queues) {
-    constexpr int R = 16;
+    constexpr int R = 16 * RT;  // query blocks per workgroup: RT MFMA row tiles
     extern __shared__ uint16_t bits16[];  // [R][NKT]: the decisions on 16-key tile kt of row r
     __shared__ float qs[R][D + 1];
     __shared__ float tau_s[R];    // the thresholds reported
@@ -464,7 +475,7 @@ __global__ void __launch_bounds__(256) route_moments_kernel(
     }
     __syncthreads();
 
-    // thresholds: wave w takes rows 4w .. 4w+3, lane l the columns l + 64 m of
+    // thresholds: wave w takes rows 4 RT w .. 4 RT w + 4 RT - 1, lane l the columns l + 64 m of
     // v = qbar_r Cov, then e_r = v . qbar_r (= sigma_r^2 / c^2) and
     // qbar_r . mbar by butterflies, all in fp64; tau_r is rounded to fp32
     // once.  sigma_r = 0 (the pooled keys all equal, or qbar_r orthogonal to
@@ -480,9 +491,9 @@ __global__ void __launch_bounds__(256) route_moments_kernel(
         const double c64 = 1.0 / __builtin_sqrt(static_cast<double>(D));
         const float* mh = mom + (size_t)h * (D + D * D);
         const float* cov = mh + D;
-        double v[4][CPL];
+        double v[4 * RT][CPL];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
+        for (int rr = 0; rr < 4 * RT; ++rr)
 #pragma unroll
             for (int m = 0; m < CPL; ++m) v[rr][m] = 0.0;
 #pragma unroll 4
@@ -491,15 +502,15 @@ __global__ void __launch_bounds__(256) route_moments_kernel(
 #pragma unroll
             for (int m = 0; m < CPL; ++m) crow[m] = static_cast<double>(cov[dp * D + lane + 64 * m]);
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const double qd = static_cast<double>(qs[4 * wave + rr][dp]);
+            for (int rr = 0; rr < 4 * RT; ++rr) {
+                const double qd = static_cast<double>(qs[4 * RT * wave + rr][dp]);
 #pragma unroll
                 for (int m = 0; m < CPL; ++m) v[rr][m] = __builtin_fma(qd, crow[m], v[rr][m]);
             }
         }
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            const int r = 4 * wave + rr;
+        for (int rr = 0; rr < 4 * RT; ++rr) {
+            const int r = 4 * RT * wave + rr;
             double e = 0.0, mu = 0.0;
 #pragma unroll
             for (int m = 0; m < CPL; ++m) {
@@ -527,13 +538,17 @@ __global__ void __launch_bounds__(256) route_moments_kernel(
     // MFMA, the same operands and order), compared as they leave the MFMA
     const int l16 = lane & 15, g = lane >> 4;
     constexpr int QD = D / 4;
-    float qv[QD];
+    float qv[RT][QD];
 #pragma unroll
-    for (int e = 0; e < QD; ++e) qv[e] = qs[l16][g * QD + e];
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int e = 0; e < QD; ++e) qv[rt][e] = qs[16 * rt + l16][g * QD + e];
     const float* kh = kbar + (size_t)h * N * D;
-    float tr[4];
+    float tr[RT][4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) tr[x] = tau_cmp[4 * g + x];
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) tr[rt][x] = tau_cmp[16 * rt + 4 * g + x];
     auto kload = [&](int kt, float (&kv)[QD]) __attribute__((always_inline)) {
         const float4* src = reinterpret_cast<const float4*>(kh + (size_t)min(kt * 16 + l16, N - 1) * D + g * QD);
 #pragma unroll
@@ -543,16 +558,23 @@ __global__ void __launch_bounds__(256) route_moments_kernel(
         }
     };
     auto decide = [&](int kt, const float (&kv)[QD]) __attribute__((always_inline)) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        f32x4_t acc[RT];
 #pragma unroll
-        for (int st = 0; st < QD; ++st) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[st], kv[st], acc, 0, 0, 0);
-        const int j = kt * 16 + l16;  // lane holds rows 4g .. 4g+3 of key j
+        for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const uint64_t m = __ballot(j < N && acc[x] * c > tr[x]);
-            // lanes 16 g' .. 16 g' + 15 hold row 4 g' + x
-            if (l16 == 0) bits16[(4 * g + x) * NKT + kt] = static_cast<uint16_t>(m >> (16 * g));
-        }
+        for (int st = 0; st < QD; ++st)
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+                acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[rt][st], kv[st], acc[rt], 0, 0, 0);
+        const int j = kt * 16 + l16;  // lane holds rows 16 rt + 4g .. 16 rt + 4g+3 of key j
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                const uint64_t m = __ballot(j < N && acc[rt][x] * c > tr[rt][x]);
+                // lanes 16 g' .. 16 g' + 15 hold row 16 rt + 4 g' + x
+                if (l16 == 0) bits16[(16 * rt + 4 * g + x) * NKT + kt] = static_cast<uint16_t>(m >> (16 * g));
+            }
     };
     float kva[QD], kvb[QD];
     if (wave < NKT) kload(wave, kva);
@@ -628,9 +650,10 @@ hipError_t route_moments_t(const float* qbar, const float* kbar, float* mom, int
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int gph = (N + 15) / 16;
-    const size_t shm = sizeof(uint16_t) * 16 * (size_t)((N + 15) / 16);
-    hipLaunchKernelGGL((route_moments_kernel<D>), dim3(H * gph), dim3(256), shm, s, qbar, kbar,
+    constexpr int RT = 2;  // 32 query blocks per workgroup (4: one wave per SIMD, slower)
+    const int gph = (N + 16 * RT - 1) / (16 * RT);
+    const size_t shm = sizeof(uint16_t) * 16 * RT * (size_t)((N + 15) / 16);
+    hipLaunchKernelGGL((route_moments_kernel<D, RT>), dim3(H * gph), dim3(256), shm, s, qbar, kbar,
                        static_cast<const float*>(mom), N, gph, c, beta, tau_in, tau, kept, sel, (N + 31) / 32,
                        queues);
     return hipGetLastError();
