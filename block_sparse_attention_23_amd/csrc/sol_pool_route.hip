@@ -666,7 +666,7 @@ hipError_t route_d(const float* qbar, const float* kbar, float* mom, int H, int 
     // as many rows per workgroup (at most one 16-row MFMA tile) as 80 KB of
     // LDS holds (two workgroups per CU share its 160 KB); threshold routing
     // with longer rows takes its statistics from the key moments instead
-    // and serves 16 rows per workgroup without holding them
+    // and serves 32 rows per workgroup without holding them
     const size_t row_bytes = sizeof(float) * (size_t)N;
     constexpr size_t kLds = 80 * 1024;
     if (topk < 0 && 16 * row_bytes > kLds)

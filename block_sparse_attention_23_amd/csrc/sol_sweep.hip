@@ -13,8 +13,9 @@
 //      keys that holds an unselected block of a query block, then one exact
 //      entry per key block that a query block selected (the union, so a key
 //      block chosen by several is loaded once; at B = 32, one 64-key tile per
-//      two consecutive key blocks of the union), each tagged with the query
-//      blocks that use it (at B = 32 each wave reads its own block's bits).
+//      two key blocks that the same query blocks selected), each tagged with
+//      the query blocks that use it (at B = 32 each wave reads its own
+//      block's bits).
 //   2. the tile loop over 64-key tiles.  Tiles stream from HBM straight into
 //      LDS (direct-to-LDS buffer loads, 16 bytes a lane) into two buffers, so
 //      the next tile loads while the current one is computed; the loads are
