@@ -109,11 +109,12 @@ def test_beta_minus_inf_equals_dense_kernel():
     assert (a.float() - b.float()).abs().max().item() <= 1e-2
 
 
-def test_deterministic_across_runs():
+@pytest.mark.parametrize("B", [32, 64, 128])
+def test_deterministic_across_runs(B):
     inp = grid_inp(4, 4000, 128, "bf16", seed=6)
     q, k, v = to_device(inp)
-    r1 = binding.attn_fwd(q, k, v, 64, 1.0, debug=True)
-    r2 = binding.attn_fwd(q, k, v, 64, 1.0, debug=True)
+    r1 = binding.attn_fwd(q, k, v, B, 1.0, debug=True)
+    r2 = binding.attn_fwd(q, k, v, B, 1.0, debug=True)
     torch.cuda.synchronize()
     for x, y in zip(r1, r2):
         assert torch.equal(x, y)
