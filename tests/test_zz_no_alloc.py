@@ -59,3 +59,36 @@ def test_noalloc_on_a_side_stream():
         binding.attn_fwd_noalloc(q, k, v, 64, 1.0, out=out, kept=kept, stream=side)
     side.synchronize()
     assert torch.equal(out, ref_out) and torch.equal(kept, ref_kept)
+
+
+@pytest.mark.parametrize("H,grid,L", [(3, (4, 16, 40), 2500), (2, (22, 64, 64), 1400 * 64 - 9)],
+                         ids=["rows-on-chip", "key-moments"])
+def test_noalloc_forward_replays_from_a_hip_graph(H, grid, L):
+    """The callers the allocation-free entry point is for include HIP graph
+    capture: sol_attn_fwd_noalloc captured on torch's capture stream and
+    replayed three times, with unrelated eager work and synchronisations
+    between the replays, reproduces the eager sol_attn_fwd result bit for
+    bit on every replay (nothing inside it allocates, clears memory from
+    the host or synchronises)."""
+    inp = gen.grid_inputs(H, grid, 128, seed=77 + H, dtype="bf16", truncate=L)
+    q, k, v = to_device(inp)
+    ref_out, ref_kept = binding.attn_fwd(q, k, v, 64, 1.0)
+    out = torch.empty_like(q)
+    kept = torch.empty_like(ref_kept)
+    binding.attn_fwd_noalloc(q, k, v, 64, 1.0, out=out, kept=kept)  # the scratch is looked up eagerly
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        binding.attn_fwd_noalloc(q, k, v, 64, 1.0, out=out, kept=kept)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(0)
+        kept.fill_(-1)
+        other = torch.randn(1 << 20, device=q.device)
+        other.mul_(2.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(kept, ref_kept), rep
+    del graph
+    torch.cuda.synchronize()
