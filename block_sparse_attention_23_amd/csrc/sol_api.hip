@@ -42,6 +42,8 @@ int check_tensors(const void* q, const void* k, const void* v, const void* out, 
 //   qbar, kbar, vsum : fp32 [H][N][d]     pooled tensors
 //   tau              : fp32 [H][N]        thresholds
 //   queues           : int32[8]           sweep work counters
+//   gcost            : u64  [H][8][P]     partial grouping costs per head and group stride
+//   gstride          : int32[H]           the group stride chosen per head
 //   kbar_bf, vsum_bf : bf16 [H][N][d]     MFMA operands of the approximate path
 //   sel              : u32  [H][N][W]     selection bits, W = ceil(N / 32)
 //   mom              : fp32 [H][2d + d*d] key moments (routing rows longer than LDS holds)
@@ -51,6 +53,8 @@ struct Workspace {
     float* vsum;
     float* tau;
     int* queues;
+    unsigned long long* gcost;
+    int* gstride;
     uint16_t* kbar_bf;
     uint16_t* vsum_bf;
     uint32_t* sel;
@@ -66,6 +70,8 @@ Workspace carve(void* base, int H, int L, int d, int B, bool lean = false) {
     const size_t pooled_bf = align_up(sizeof(uint16_t) * (size_t)H * N * d);
     const size_t taub = align_up(sizeof(float) * (size_t)H * N);
     const size_t qb = align_up(sizeof(int) * 8);
+    const size_t gcb = align_up(sizeof(unsigned long long) * (size_t)H * 8 * sol::group_cost_parts((int)N, B));
+    const size_t gsb = align_up(sizeof(int) * (size_t)H);
     const size_t selb = align_up(sizeof(uint32_t) * (size_t)H * N * ((N + 31) / 32));
     const size_t momb = align_up(sizeof(float) * (size_t)H * ((size_t)d + (size_t)d * d));
     char* p = static_cast<char*>(base);
@@ -76,6 +82,8 @@ Workspace carve(void* base, int H, int L, int d, int B, bool lean = false) {
     w.vsum = lean ? nullptr : reinterpret_cast<float*>(p + off); off += lean ? 0 : pooled;
     w.tau = reinterpret_cast<float*>(p + off); off += taub;
     w.queues = reinterpret_cast<int*>(p + off); off += qb;
+    w.gcost = reinterpret_cast<unsigned long long*>(p + off); off += gcb;
+    w.gstride = reinterpret_cast<int*>(p + off); off += gsb;
     w.kbar_bf = reinterpret_cast<uint16_t*>(p + off); off += pooled_bf;
     w.vsum_bf = reinterpret_cast<uint16_t*>(p + off); off += pooled_bf;
     w.sel = reinterpret_cast<uint32_t*>(p + off); off += selb;
@@ -91,7 +99,8 @@ hipError_t launch_sweep(const sol::AttnArgs& a, int bf16, int d, int B, bool den
 sol::AttnArgs sweep_args(const void* q, const void* k, const void* v, const float* qbar,
                          const float* kbar, const float* vsum, const float* tau,
                          const uint16_t* kbar_bf, const uint16_t* vsum_bf, int H, int L, int d,
-                         int B, void* out, int* counters, const uint32_t* sel) {
+                         int B, void* out, int* counters, unsigned long long* gcost,
+                         int* gstride, const uint32_t* sel) {
     const int N = (L + B - 1) / B;
     sol::AttnArgs a = {};
     a.q = q; a.k = k; a.v = v;
@@ -100,6 +109,8 @@ sol::AttnArgs sweep_args(const void* q, const void* k, const void* v, const floa
     a.out = out;
     a.sel = sel;
     a.queues = counters;
+    a.gcost = gcost;
+    a.gstride = gstride;
     a.H = H; a.L = L; a.N = N; a.W = (N + 31) / 32;
     a.nlast = L - (N - 1) * B;
     a.c = static_cast<float>(1.0 / sqrt(static_cast<double>(d)));
@@ -147,7 +158,7 @@ int launch_forward(const void* q, const void* k, const void* v, int H, int L, in
                           topk, w.mom) != hipSuccess)
         return SOL_EHIP;
     sol::AttnArgs a = sweep_args(q, k, v, w.qbar, w.kbar, w.vsum, tau, w.kbar_bf, w.vsum_bf, H, L,
-                                 d, B, out, w.queues, sel);
+                                 d, B, out, w.queues, w.gcost, w.gstride, sel);
     a.drop_approx = (flags & SOL_DROP_APPROX) ? 1 : 0;
     if (launch_sweep(a, bf16, d, B, false, s) != hipSuccess) return SOL_EHIP;
     return SOL_OK;
@@ -296,7 +307,7 @@ int sol_sweep(const void* q, const void* k, const void* v, const float* qbar, co
         sel = dst;
     }
     const sol::AttnArgs a = sweep_args(q, k, v, qbar, kbar, vsum, tau, w.kbar_bf, w.vsum_bf, H, L,
-                                       d, B, out, w.queues, sel);
+                                       d, B, out, w.queues, w.gcost, w.gstride, sel);
     if (launch_sweep(a, bf16, d, B, false, s) != hipSuccess) return SOL_EHIP;
     return SOL_OK;
 }
@@ -324,7 +335,7 @@ int sol_sweep_timed(const void* q, const void* k, const void* v, const float* qb
         hipSuccess)
         return SOL_EHIP;
     sol::AttnArgs a = sweep_args(q, k, v, qbar, kbar, vsum, tau, w.kbar_bf, w.vsum_bf, H, L, d, B, out,
-                                 w.queues, sel_bits);
+                                 w.queues, w.gcost, w.gstride, sel_bits);
     a.order = order;
     a.trace = reinterpret_cast<unsigned long long*>(item_clock);
     if (launch_sweep(a, 1, d, B, false, s) != hipSuccess) return SOL_EHIP;

@@ -19,6 +19,11 @@ struct AttnArgs {
     void* out;
     const uint32_t* sel; // [H][N][W] selection bits of the routing kernel (bf16 sweep)
     int* queues;         // 8 per-XCD work counters (sol only)
+    // bf16 sweep, query-block grouping: scratch for the partial grouping
+    // costs (H * 8 * group_cost_parts(N, B) entries) and the chosen group
+    // stride per head (H entries); gcost null: consecutive groups
+    unsigned long long* gcost;
+    int* gstride;
     int H, L, N, W;
     int nlast;           // valid tokens in the last block
     float c;             // 1/sqrt(d): proxy-score scale
@@ -46,6 +51,8 @@ hipError_t launch_route(const float* qbar, const float* kbar, int H, int N, int 
                         float beta, const float* tau_in, float* tau, int32_t* kept, uint32_t* sel,
                         int* queues, hipStream_t s, int topk = -1, float* mom = nullptr);
 hipError_t launch_sweep_bf16(const AttnArgs& a, int d, int B, bool dense, hipStream_t s);
+// Partial grouping costs per (head, stride) that the bf16 sweep writes.
+int group_cost_parts(int N, int B);
 hipError_t launch_attn_f32(const AttnArgs& a, int d, int B, bool dense, hipStream_t s);
 hipError_t launch_reset_counters(int* queues, hipStream_t s);
 

@@ -1,9 +1,11 @@
 // sol_sweep.hip -- the fused Sol-Attn sweep for bf16 inputs on gfx950.
 //
-// A workgroup (4 waves) owns 128 query rows at a time: four 32-row query
-// blocks (B = 32), two 64-row blocks (B = 64) or one 128-row block
-// (B = 128).  Wave w owns rows 32w .. 32w+31 as two 16-row tiles of
-// v_mfma_f32_16x16x32_bf16.
+// A workgroup (4 waves) owns a group of 128 query rows at a time: four
+// 32-row query blocks (B = 32), two 64-row blocks (B = 64) or one 128-row
+// block (B = 128); the blocks of a group are consecutive or, where the
+// selection favours it, spaced by a per-head group stride (group_map below).
+// Wave w owns 32 rows of the group (rows 32w .. 32w+31 of consecutive
+// blocks) as two 16-row tiles of v_mfma_f32_16x16x32_bf16.
 //
 // Per workgroup ("Sol-Attn" visual explainer, "The complete idea in one
 // pass", Eq. (4), Eq. (9), Eq. (10), Eq. (11)):
@@ -34,11 +36,11 @@
 //      masked.  One running max / denominator / accumulator serves both.
 //   3. out = O / l, rounded to bf16.
 //
-// Scheduling: persistent workgroups pull 128-row groups from eight work
-// queues, one per XCD (workgroup w runs on XCD w % 8).  Queue x holds, head
-// by head, the groups [x G / 8, (x+1) G / 8) of the head's G groups, so the
-// workgroups of one XCD work on neighbouring rows of the same head at the
-// same time and share its L2.  Every workgroup exits once all eight queues
+// Scheduling: persistent workgroups pull groups from eight work queues, one
+// per XCD (workgroup w runs on XCD w % 8).  Queue x holds, head by head, the
+// groups [x G / 8, (x+1) G / 8) of the head's G groups, so the workgroups of
+// one XCD work on neighbouring rows of the same head at the same time and
+// share its L2.  Every workgroup exits once all eight queues
 // are drained.  Dense mode: every key block exact, no routing, one group per
 // workgroup.
 #include <hip/hip_runtime.h>
@@ -64,6 +66,94 @@ struct Sweep : TileLayout<D> {
     static constexpr int PB = QB < 2 ? 2 : QB;
     static constexpr int PS = 31 - PB;
 };
+
+// Query-block groups.  A workgroup item holds QB = 128 / B query blocks of
+// one head.  With group stride s, the head's blocks are cut into runs of
+// QB s blocks, and group r of a run holds blocks r, r + s, ..., r + (QB-1) s
+// of it; the blocks after the last whole run form groups of consecutive
+// blocks.  Stride 1 is plain consecutive grouping.  Where each row of a video
+// latent's frame spans s query blocks, stride s puts blocks of neighbouring
+// rows at the same horizontal position into one group; their selections
+// overlap more than those of side-by-side blocks of one row, and the group's
+// union tile list is shorter.  The stride is chosen per head from the
+// selection bits by group_cost_kernel.
+struct GroupMap {
+    int blk0, bstep, nqb;  // block b < nqb of the group is blk0 + b * bstep
+};
+
+template <int QB>
+__device__ __forceinline__ GroupMap group_map(int gi, int N, int st) {
+    const int span = QB * st;
+    const int full = (N / span) * span;
+    const int nfg = full / QB;  // groups inside whole runs
+    if (gi < nfg) return GroupMap{(gi / st) * span + gi % st, st, QB};
+    const int b0 = full + (gi - nfg) * QB;
+    return GroupMap{b0, 1, min(QB, N - b0)};
+}
+
+constexpr int kMaxStride = 8;  // candidate group strides 1 .. kMaxStride
+constexpr int kCostGroups = 64;  // groups per workgroup of group_cost_kernel
+
+// Grouping cost of a head at a stride: the sum over the head's groups of the
+// number of key blocks that any of the group's query blocks selected (the
+// exact entries of its union tile list).  Workgroup (h, s, p) sums groups
+// p kCostGroups .. (p+1) kCostGroups - 1 of head h at stride s + 1 into
+// part[(h kMaxStride + s) P + p], P = ceil(G / kCostGroups); a wave takes
+// every fourth of them, its lanes over the selection words.
+template <int QB>
+__global__ void __launch_bounds__(256) group_cost_kernel(const uint32_t* __restrict__ sel, int N, int W, int P,
+                                                         unsigned long long* __restrict__ part) {
+    __shared__ unsigned long long wsum[4];
+    const int p = blockIdx.x % P, hs = blockIdx.x / P;
+    const int h = hs / kMaxStride, st = hs % kMaxStride + 1;
+    const int NG = (N + QB - 1) / QB;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint32_t* sh = sel + (size_t)h * N * W;
+    unsigned long long cnt = 0;
+    const int g1 = min(NG, (p + 1) * kCostGroups);
+    // four groups at a time, so that their loads are in flight together
+    for (int gb = p * kCostGroups + wave; gb < g1; gb += 16) {
+        GroupMap gm[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+            gm[x] = gb + 4 * x < g1 ? group_map<QB>(gb + 4 * x, N, st) : GroupMap{0, 0, 0};
+        for (int w = lane; w < W; w += 64) {
+            uint32_t u[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int b = 0; b < QB; ++b)
+                    if (b < gm[x].nqb) u[x] |= sh[(size_t)(gm[x].blk0 + b * gm[x].bstep) * W + w];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) cnt += (unsigned long long)__popc(u[x]);
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
+    if (lane == 0) wsum[wave] = cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) part[blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+}
+
+// The group stride of head h = blockIdx.x: the one of least summed cost, the
+// smallest on a tie (one wave).
+__global__ void __launch_bounds__(64) group_pick_kernel(const unsigned long long* __restrict__ part, int P,
+                                                        int* __restrict__ stride) {
+    const int h = blockIdx.x, lane = threadIdx.x;
+    unsigned long long best = 0;
+    int bs = 1;
+    for (int s = 0; s < kMaxStride; ++s) {
+        unsigned long long c = 0;
+        for (int p = lane; p < P; p += 64) c += part[((size_t)h * kMaxStride + s) * P + p];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+        if (s == 0 || c < best) {
+            best = c;
+            bs = s + 1;
+        }
+    }
+    if (lane == 0) stride[h] = bs;
+}
 
 template <int D, int BLK, bool DENSE>
 __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
@@ -157,9 +247,12 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             prev_item = item;
         }
         const int h = item / NG, gi = item % NG;
-        const int i0 = gi * S::QB;
-        const int nqb = min(S::QB, N - i0);  // valid query blocks in this group
-        const int q0 = gi * 128;
+        // the head's group stride (group_pick_kernel)
+        const int st = (!DENSE && S::QB > 1 && a.gcost) ? a.gstride[h] : 1;
+        const GroupMap gm = group_map<S::QB>(gi, N, st);
+        const int nqb = gm.nqb;  // valid query blocks in this group
+        // first row of this wave's 32 (rows of query block myb of the group)
+        const int r0 = (gm.blk0 + myb * gm.bstep) * BLK + (wave * 32) % BLK;
         const size_t head_off = (size_t)h * L * D;
 
         int T;
@@ -171,7 +264,7 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             // routing kernel: bit j of block i is s_ij > tau_i)
             for (int t = tid; t < S::QB * nwords; t += S::NT) {
                 const int b = t / nwords, w = t % nwords;
-                selbits[t] = b < nqb ? a.sel[((size_t)h * N + i0 + b) * a.W + w] : 0u;
+                selbits[t] = b < nqb ? a.sel[((size_t)h * N + gm.blk0 + b * gm.bstep) * a.W + w] : 0u;
             }
             __syncthreads();
             if (wave == 0) {
@@ -268,11 +361,11 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             T = __builtin_amdgcn_readfirstlane(misc_s[1]);
         }
 
-        // Q fragments (B operand of S^T = K Q^T): rows q0 + 32w + 16qt + l16
+        // Q fragments (B operand of S^T = K Q^T): rows r0 + 16qt + l16
         bf16x8_t qf[2][S::NS];
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
-            const int row = q0 + wave * 32 + qt * 16 + l16;
+            const int row = r0 + qt * 16 + l16;
             const u16* src = qg + head_off + (size_t)row * D + g * 8;
 #pragma unroll
             for (int s = 0; s < S::NS; ++s)
@@ -577,7 +670,7 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                 // row 0 of the weight tile sits in element 0 of lanes 0..15
                 const float lt = __shfl(o[S::NDT][qt][0], l16);
                 const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;  // 0: nothing kept (keep-or-drop)
-                const int row = q0 + wave * 32 + qt * 16 + l16;
+                const int row = r0 + qt * 16 + l16;
                 if (row < L) {
                     u16* dst = og + head_off + (size_t)row * D + g * 4;
 #pragma unroll
@@ -596,6 +689,15 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
 // ============================================================================
 // launcher
 // ============================================================================
+namespace {
+
+}  // namespace
+
+int group_cost_parts(int N, int B) {
+    const int NG = (N + 128 / B - 1) / (128 / B);
+    return (NG + kCostGroups - 1) / kCostGroups;
+}
+
 namespace {
 
 int device_cus() {
@@ -626,6 +728,14 @@ hipError_t sweep_t(const AttnArgs& a, hipStream_t s) {
             per_cu < 1)
             per_cu = 1;
         grid = device_cus() * per_cu;
+    }
+    if (!DENSE && S::QB > 1 && a.gcost) {
+        const int P = group_cost_parts(a.N, BLK);
+        hipLaunchKernelGGL((group_cost_kernel<S::QB>), dim3(a.H * kMaxStride * P), dim3(256), 0, s, a.sel, a.N,
+                           a.W, P, a.gcost);
+        hipLaunchKernelGGL(group_pick_kernel, dim3(a.H), dim3(64), 0, s, a.gcost, P, a.gstride);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3(grid), dim3(S::NT), dyn, s, a);
     return hipGetLastError();

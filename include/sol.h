@@ -133,8 +133,10 @@ int sol_sweep(const void* q, const void* k, const void* v,
  * in a caller-given order instead of from the per-XCD queues.  The abstract
  * notes that selection gives query blocks "dynamic but potentially
  * imbalanced budgets"; this measures what the claim order does about it.
- * A group item is one workgroup's 128 query rows of one head: item
- * h * G + g for g < G = ceil(N / (128 / B)) (B = 64: pairs of query blocks).
+ * A group item is one workgroup's 128 / B query blocks of one head: item
+ * h * G + g for g < G = ceil(N / (128 / B)) (B = 64: pairs of query blocks;
+ * which blocks form group g depends on the head's group stride, chosen from
+ * the selection: see sol_attn_fwd).
  * order      : DEVICE int32 [H*G], a permutation of 0 .. H*G-1 (claimed in
  *              that order by one counter), or NULL for the per-XCD queues.
  *              An entry outside 0 .. H*G-1 ends the claiming workgroup.
@@ -165,6 +167,13 @@ int sol_sweep_timed(const void* q, const void* k, const void* v,
  *           / (sum_{j in U} n_j e^{g_j}   + sum_{S} sum_t e^{a})
  * Proxy scores exist only on chip; they are never written to memory.
  * Equivalent to sol_pool, then sol_route, then sol_sweep on one stream.
+ * Work layout (bf16 sweep): query blocks go in groups of 128 / B that share
+ * one list of key tiles, the union of their selections.  Per head a group
+ * holds consecutive blocks, or blocks spaced by a group stride s in 2..8
+ * (runs of (128 / B) s blocks, group r of a run holding blocks r, r + s, ...;
+ * consecutive groups after the last whole run) when that stride gives the
+ * smallest summed union size (ties: the smaller stride).  The grouping
+ * changes only the order in which a row's terms are accumulated.
  *
  * beta        : any float except NaN (+-INFINITY allowed).
  * out         : DEVICE [H][L][d], dtype dt.

@@ -62,6 +62,46 @@ def test_forward_bf16_unstructured(beta):
     run_and_check(inp, 64, beta)
 
 
+def grouping_cost(bits, QB, st):
+    """Host model of the sweep's grouping cost at group stride st: over every
+    head, the number of key blocks selected by any query block of a group,
+    summed over the groups that stride forms (runs of QB st blocks, group r of
+    a run holding blocks r, r + st, ...; consecutive groups after the last
+    whole run).  bits: the selection mask [H][N][W] (uint32)."""
+    H, N, _ = bits.shape
+    span = QB * st
+    full = (N // span) * span
+    groups = [[a + r + k * st for k in range(QB)] for a in range(0, full, span) for r in range(st)]
+    groups += [list(range(i, min(i + QB, N))) for i in range(full, N, QB)]
+    assert sorted(b for g in groups for b in g) == list(range(N))
+    tot = 0
+    for h in range(H):
+        for g in groups:
+            u = np.bitwise_or.reduce(bits[h, g], axis=0)
+            tot += int(np.unpackbits(u.view(np.uint8)).sum())
+    return tot
+
+
+@pytest.mark.parametrize("B,grid,L,d", [(32, (2, 16, 64), 2000, 128), (32, (2, 32, 64), 4000, 64),
+                                        (32, (2, 32, 96), 6000, 128), (64, (2, 8, 128), 2000, 128),
+                                        (64, (2, 16, 128), 4000, 64)])
+def test_forward_strided_groups(B, grid, L, d):
+    """Frames whose rows span several query blocks: the selection makes a
+    group stride above 1 the cheapest, so the sweep groups blocks of
+    neighbouring rows instead of consecutive ones (ragged last block, and
+    groups of consecutive blocks after the last whole run).  Every element
+    against the oracle."""
+    inp = gen.grid_inputs(2, grid, d, 11, "bf16", truncate=L)
+    q, k, v = to_device(inp)
+    out, kept, mask, tau = binding.attn_fwd(q, k, v, B, 1.0, debug=True)
+    torch.cuda.synchronize()
+    bits = mask.cpu().numpy().view(np.uint32)
+    costs = [grouping_cost(bits, 128 // B, st) for st in range(1, 9)]
+    assert int(np.argmin(costs)) + 1 > 1, costs
+    s = check_result(inp, B, 1.0, out, kept, mask)
+    assert 0.0 < s["kept_frac"] < 1.0
+
+
 @pytest.mark.parametrize("beta", [-INF, 0.0, 1.0, INF])
 @pytest.mark.parametrize("d,B,L", [(64, 64, 1024), (128, 64, 333), (64, 128, 1000), (128, 32, 1000),
                                    (64, 32, 333), (128, 128, 1000), (128, 128, 256)])
