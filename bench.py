@@ -272,6 +272,47 @@ def ablation(args, np, torch, binding, gen):
                       "error": "relative L2 over all outputs", "rows": rows}))
 
 
+def sweep_groups(sel, QB, np):
+    """The bf16 sweep's query-block groups of one head (the rule stated at
+    sol_attn_fwd in include/sol.h): group stride st in 1..8 with the
+    smallest summed union size of the groups' selections, the smaller stride
+    on a tie; runs of QB st blocks, group r of a run holding blocks r, r + st,
+    ...; consecutive groups after the last whole run.  sel: [N][N] bool.
+    Returns (st, list of block-index lists in group order)."""
+    N = sel.shape[0]
+
+    def groups(st):
+        span = QB * st
+        full = (N // span) * span
+        gs = [[a + r + k * st for k in range(QB)] for a in range(0, full, span) for r in range(st)]
+        return gs + [list(range(i, min(i + QB, N))) for i in range(full, N, QB)]
+
+    best = None
+    for st in range(1, 9):
+        gs = groups(st)
+        c = sum(int(sel[g].any(axis=0).sum()) for g in gs)
+        if best is None or c < best[0]:
+            best = (c, st, gs)
+    return best[1], best[2]
+
+
+def group_tiles(sel_g, B, TB, np):
+    """64-key steps of one group's tile list: approximate chunks of TB pooled
+    keys holding an unselected block of a member, then the exact tiles (B >=
+    64: one per selected key block of the union, B / 64 steps each; B = 32:
+    key blocks chosen by the same members pair up, ceil(count / 2) tiles per
+    membership mask).  sel_g: [members][N] bool."""
+    N = sel_g.shape[1]
+    NC = -(-N // TB)
+    unsel = ~np.pad(sel_g, ((0, 0), (0, NC * TB - N)), constant_values=True).reshape(len(sel_g), NC, TB)
+    approx = int(unsel.any(axis=2).any(axis=0).sum()) * (TB // 64)
+    if B >= 64:
+        return approx + int(sel_g.any(axis=0).sum()) * (B // 64)
+    masks = (sel_g * (1 << np.arange(len(sel_g)))[:, None]).sum(axis=0)
+    counts = np.bincount(masks, minlength=1 << len(sel_g))[1:]
+    return approx + int(((counts + 1) // 2).sum())
+
+
 def schedule(args, np, torch, binding, gen):
     """Load balance of the sweep's persistent workgroups ("dynamic but
     potentially imbalanced budgets"): for each beta, the sweep kernel runs
@@ -303,17 +344,16 @@ def schedule(args, np, torch, binding, gen):
     for beta in betas:
         tau, kept = binding.route(qbar, kbar, L, B, beta, sel_bits=bits, workspace=ws)
         sel = binding.unpack_mask(bits, N).astype(bool)  # [H][N][N]
-        pad = G * QB - N
-        selg = np.pad(sel, ((0, 0), (0, pad), (0, 0))).reshape(H, G, QB, N)
-        exact = selg.any(axis=2).sum(axis=2)  # union of the group's selections, key blocks
-        exact_tiles = exact * (B // 64) if B >= 64 else (exact + 1) // 2
-        padk = NC * TB - N
-        unsel = ~np.pad(sel, ((0, 0), (0, pad), (0, padk)), constant_values=True).reshape(H, G, QB, NC, TB)
-        approx_tiles = unsel.any(axis=4).any(axis=2).sum(axis=2) * (TB // 64)
-        cost = (exact_tiles + approx_tiles).reshape(-1)
+        cost, strides = [], []
+        for h in range(H):
+            st, gs = sweep_groups(sel[h], QB, np)
+            strides.append(st)
+            cost += [group_tiles(sel[h][g], B, TB, np) for g in gs]
+        cost = np.array(cost)
         lpt = torch.from_numpy(np.argsort(-cost, kind="stable").astype(np.int32)).cuda()
         res = {"beta": beta, "kept_frac": float(sel.mean()), "items": int(H * G),
-               "tiles_per_item": {"mean": float(cost.mean()), "min": int(cost.min()), "max": int(cost.max())}}
+               "tiles_per_item": {"mean": float(cost.mean()), "min": int(cost.min()), "max": int(cost.max())},
+               "group_strides": {str(x): strides.count(x) for x in sorted(set(strides))}}
         for name, order in (("xcd_queues", None), ("longest_first", lpt)):
             fn = lambda: binding.sweep_timed(q, k, v, qbar, kbar, vsum, tau, B, bits, order=order, out=out,
                                              workspace=ws)
