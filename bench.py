@@ -225,6 +225,8 @@ def ablation(args, np, torch, binding, gen):
     """What the approximate correction buys: for each beta, relative L2 error
     against the in-library dense attention and time per forward of
       sol        Sol-Attn (threshold selection, approximate correction),
+      fused_route  the same, its decisions taken inside the sweep from the
+                 Eq. (5) thresholds (SOL_FUSED_ROUTE),
       drop       the same selection, unselected blocks left out (keep-or-drop),
       topk       a fixed budget of round(rho N) blocks per query block, rho =
                  Sol-Attn's kept fraction at that beta, with the correction,
@@ -251,13 +253,15 @@ def ablation(args, np, torch, binding, gen):
         rho = kept.sum().item() / (w.H * w.N * w.N)
         runs = {
             "sol": lambda: binding.attn_fwd(q, k, v, w.B, beta, out=out, workspace=ws),
+            "fused_route": lambda: binding.attn_fwd_variant(q, k, v, w.B, beta, fused_route=True,
+                                                            out=out, workspace=ws, debug=False),
             "drop": lambda: binding.attn_fwd_variant(q, k, v, w.B, beta, drop_approx=True,
-                                                     out=out, workspace=ws),
+                                                     out=out, workspace=ws, debug=False),
             "topk": lambda: binding.attn_fwd_variant(q, k, v, w.B, beta, keep_frac=rho, topk=True,
-                                                     out=out, workspace=ws),
+                                                     out=out, workspace=ws, debug=False),
             "topk_drop": lambda: binding.attn_fwd_variant(q, k, v, w.B, beta, keep_frac=rho,
                                                           topk=True, drop_approx=True, out=out,
-                                                          workspace=ws),
+                                                          workspace=ws, debug=False),
         }
         row = {"beta": beta, "kept_frac": rho}
         for name, fn in runs.items():

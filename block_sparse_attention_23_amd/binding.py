@@ -13,7 +13,7 @@ import torch
 from . import build as _build
 
 SOL_BF16, SOL_F32 = 0, 1
-SOL_DROP_APPROX, SOL_TOPK = 1, 2
+SOL_DROP_APPROX, SOL_TOPK, SOL_FUSED_ROUTE = 1, 2, 4
 
 _FUNCS = {
     "sol_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int] * 4),
@@ -270,11 +270,14 @@ def attn_fwd_noalloc(q, k, v, B, beta, out=None, kept=None, stream=None):
 
 
 def attn_fwd_variant(q, k, v, B, beta, keep_frac=0.0, drop_approx=False, topk=False, out=None,
-                     kept=None, workspace=None, stream=None):
+                     kept=None, workspace=None, stream=None, fused_route=False, debug=True):
     """The forward pass with the pages' comparators (bf16): drop_approx leaves
     the unselected blocks out (keep-or-drop); topk selects the
     round(keep_frac * N) largest proxies of every query block instead of the
-    threshold.  Returns (out, kept_counts, sel_mask bits, tau)."""
+    threshold; fused_route takes the decisions inside the sweep, from the
+    Eq. (5) thresholds (SOL_FUSED_ROUTE).  Returns (out, kept_counts,
+    sel_mask bits, tau); with debug=False the last two are None and nothing
+    records them."""
     H, L, d = _tokens(q, k, v)
     N = nblocks(L, B)
     with _on(stream, q.device):
@@ -284,14 +287,16 @@ def attn_fwd_variant(q, k, v, B, beta, keep_frac=0.0, drop_approx=False, topk=Fa
             kept = torch.empty((H, N), dtype=torch.int32, device=q.device)
         if workspace is None:
             workspace = alloc_workspace(H, L, d, B, q.device)
-        mask = torch.zeros((H, N, (N + 31) // 32), dtype=torch.int32, device=q.device)
-        tau = torch.empty((H, N), dtype=torch.float32, device=q.device)
-    flags = (SOL_DROP_APPROX if drop_approx else 0) | (SOL_TOPK if topk else 0)
+        mask = torch.zeros((H, N, (N + 31) // 32), dtype=torch.int32, device=q.device) if debug else None
+        tau = torch.empty((H, N), dtype=torch.float32, device=q.device) if debug else None
+    flags = ((SOL_DROP_APPROX if drop_approx else 0) | (SOL_TOPK if topk else 0) |
+             (SOL_FUSED_ROUTE if fused_route else 0))
     with torch.cuda.device(q.device):
         _check("sol_attn_fwd_variant", lib().sol_attn_fwd_variant(
             q.data_ptr(), k.data_ptr(), v.data_ptr(), H, L, d, B, float(beta), float(keep_frac),
             flags, _dtype_code(q), out.data_ptr(), kept.data_ptr(), workspace.data_ptr(),
-            workspace.numel(), _stream_ptr(stream, q.device), mask.data_ptr(), tau.data_ptr()))
+            workspace.numel(), _stream_ptr(stream, q.device), mask.data_ptr() if debug else None,
+            tau.data_ptr() if debug else None))
     return out, kept, mask, tau
 
 

@@ -41,6 +41,7 @@ int check_tensors(const void* q, const void* k, const void* v, const void* out, 
 // Workspace layout (each region 256-byte aligned):
 //   qbar, kbar, vsum : fp32 [H][N][d]     pooled tensors
 //   tau              : fp32 [H][N]        thresholds
+//   tau_cmp          : fp32 [H][N]        thresholds compared with, for sweeps that route inside
 //   queues           : int32[8]           sweep work counters
 //   gcost            : u64  [H][8][P]     partial grouping costs per head and group stride
 //   gstride          : int32[H]           the group stride chosen per head
@@ -52,6 +53,7 @@ struct Workspace {
     float* kbar;
     float* vsum;
     float* tau;
+    float* tau_cmp;
     int* queues;
     unsigned long long* gcost;
     int* gstride;
@@ -81,6 +83,7 @@ Workspace carve(void* base, int H, int L, int d, int B, bool lean = false) {
     w.kbar = reinterpret_cast<float*>(p + off); off += pooled;
     w.vsum = lean ? nullptr : reinterpret_cast<float*>(p + off); off += lean ? 0 : pooled;
     w.tau = reinterpret_cast<float*>(p + off); off += taub;
+    w.tau_cmp = reinterpret_cast<float*>(p + off); off += taub;
     w.queues = reinterpret_cast<int*>(p + off); off += qb;
     w.gcost = reinterpret_cast<unsigned long long*>(p + off); off += gcb;
     w.gstride = reinterpret_cast<int*>(p + off); off += gsb;
@@ -126,7 +129,8 @@ int check_forward(const void* q, const void* k, const void* v, int H, int L, int
     st = check_tensors(q, k, v, out, dt);
     if (st != SOL_OK) return st;
     if (!kept || !aligned(kept, 4) || isnan(beta)) return SOL_EINVAL;
-    if (flags & ~(unsigned)(SOL_DROP_APPROX | SOL_TOPK)) return SOL_EINVAL;
+    if (flags & ~(unsigned)(SOL_DROP_APPROX | SOL_TOPK | SOL_FUSED_ROUTE)) return SOL_EINVAL;
+    if ((flags & SOL_TOPK) && (flags & SOL_FUSED_ROUTE)) return SOL_EINVAL;
     if ((flags & SOL_TOPK) && !(keep_frac >= 0.0f && keep_frac <= 1.0f)) return SOL_EINVAL;
     if (flags && dt != SOL_BF16) return SOL_EUNSUPPORTED;
     if ((sel_mask && !aligned(sel_mask, 4)) || (tau_out && !aligned(tau_out, 4))) return SOL_EINVAL;
@@ -149,6 +153,21 @@ int launch_forward(const void* q, const void* k, const void* v, int H, int L, in
     if (sol::launch_pool(q, k, v, bf16, H, L, d, B, w.qbar, w.kbar, w.vsum,
                          bf16 ? w.kbar_bf : nullptr, bf16 ? w.vsum_bf : nullptr, s) != hipSuccess)
         return SOL_EHIP;
+    if (flags & SOL_FUSED_ROUTE) {
+        // thresholds first; the sweep routes, counts and (if asked) records
+        // its decisions itself
+        if (sol::launch_thresholds(w.qbar, w.kbar, H, N, d, c, beta, tau, w.tau_cmp, w.mom, w.queues, s) !=
+            hipSuccess)
+            return SOL_EHIP;
+        sol::AttnArgs a = sweep_args(q, k, v, w.qbar, w.kbar, w.vsum, tau, w.kbar_bf, w.vsum_bf, H, L,
+                                     d, B, out, w.queues, nullptr, nullptr, nullptr);
+        a.tau_cmp = w.tau_cmp;
+        a.kept_out = kept;
+        a.sel_out = sel_mask;
+        a.drop_approx = (flags & SOL_DROP_APPROX) ? 1 : 0;
+        if (launch_sweep(a, bf16, d, B, false, s) != hipSuccess) return SOL_EHIP;
+        return SOL_OK;
+    }
     // fixed budget: round(keep_frac * N), halves up, within [0, N]
     const int topk = (flags & SOL_TOPK)
                          ? static_cast<int>(fmin((double)N, fmax(0.0, floor((double)keep_frac * N + 0.5))))

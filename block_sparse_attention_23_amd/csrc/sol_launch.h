@@ -29,6 +29,12 @@ struct AttnArgs {
     float c;             // 1/sqrt(d): proxy-score scale
     float c_log2e;       // 1/sqrt(d) * log2(e): attention logits in base 2
     int drop_approx;     // bf16 sweep: leave the unselected blocks out (keep-or-drop)
+    // bf16 sweep routing inside (tau_cmp not null; sel then unused): the
+    // thresholds compared with [H][N], and where the sweep writes its
+    // kept counts [H][N] and, if not null, its decision bits [H][N][W]
+    const float* tau_cmp;
+    int32_t* kept_out;
+    uint32_t* sel_out;
     // bf16 sweep, for scheduling measurements (both null in the forward pass):
     const int* order;          // [H G] group items in claim order, or null: the per-XCD queues
     unsigned long long* trace; // [H G][3] per item: claim time, end time (100 MHz clock), workgroup
@@ -50,6 +56,12 @@ hipError_t launch_pooled_to_bf16(const float* kbar, const float* vsum, size_t n,
 hipError_t launch_route(const float* qbar, const float* kbar, int H, int N, int d, float c,
                         float beta, const float* tau_in, float* tau, int32_t* kept, uint32_t* sel,
                         int* queues, hipStream_t s, int topk = -1, float* mom = nullptr);
+// Eq. (5) thresholds without decisions (for sweeps that route inside):
+// tau [H][N] as reported, tau_cmp [H][N] the thresholds the decisions compare
+// with (+inf where sigma_i = 0); mom as for launch_route; also clears the
+// sweep's work counters.
+hipError_t launch_thresholds(const float* qbar, const float* kbar, int H, int N, int d, float c, float beta,
+                             float* tau, float* tau_cmp, float* mom, int* queues, hipStream_t s);
 hipError_t launch_sweep_bf16(const AttnArgs& a, int d, int B, bool dense, hipStream_t s);
 // Partial grouping costs per (head, stride) that the bf16 sweep writes.
 int group_cost_parts(int N, int B);

@@ -457,7 +457,7 @@ __global__ void __launch_bounds__(256) route_moments_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kbar, const float* __restrict__ mom,
     int N, int groups_per_head, float c, float beta, const float* __restrict__ tau_in,
     float* __restrict__ tau_out, int32_t* __restrict__ kept, uint32_t* __restrict__ sel, int W,
-    int* __restrict__ queues) {
+    int* __restrict__ queues, float* __restrict__ tau_cmp_out, int with_decisions) {
     constexpr int R = 16 * RT;  // query blocks per workgroup: RT MFMA row tiles
     extern __shared__ uint16_t bits16[];  // [R][NKT]: the decisions on 16-key tile kt of row r
     __shared__ float qs[R][D + 1];
@@ -533,6 +533,15 @@ __global__ void __launch_bounds__(256) route_moments_kernel(
         }
     }
     __syncthreads();
+    // thresholds only (decisions taken later, inside the sweep): tau_i as
+    // reported and the threshold the decisions compare with
+    if (!with_decisions) {
+        for (int r = tid; r < nr; r += 256) {
+            tau_out[(size_t)h * N + i0 + r] = tau_s[r];
+            tau_cmp_out[(size_t)h * N + i0 + r] = tau_cmp[r];
+        }
+        return;
+    }
 
     // decisions: the proxy scores as the row-holding route forms them (fp32
     // MFMA, the same operands and order), compared as they leave the MFMA
@@ -655,7 +664,29 @@ hipError_t route_moments_t(const float* qbar, const float* kbar, float* mom, int
     const size_t shm = sizeof(uint16_t) * 16 * RT * (size_t)((N + 15) / 16);
     hipLaunchKernelGGL((route_moments_kernel<D, RT>), dim3(H * gph), dim3(256), shm, s, qbar, kbar,
                        static_cast<const float*>(mom), N, gph, c, beta, tau_in, tau, kept, sel, (N + 31) / 32,
-                       queues);
+                       queues, static_cast<float*>(nullptr), 1);
+    return hipGetLastError();
+}
+
+// Eq. (5) thresholds alone: the key moments (finite beta), then tau_i and
+// the compared threshold per query block, without scores or decisions.
+template <int D>
+hipError_t thresholds_t(const float* qbar, const float* kbar, float* mom, int H, int N, float c, float beta,
+                        float* tau, float* tau_cmp, int* queues, hipStream_t s) {
+    if (!isinf(beta)) {
+        if (!mom) return hipErrorInvalidValue;
+        hipLaunchKernelGGL((key_moments_kernel<D>), dim3(H * (D / 32) * (D / 32)), dim3(256), 0, s, kbar, N,
+                           mom);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    constexpr int RT = 2;
+    const int gph = (N + 16 * RT - 1) / (16 * RT);
+    const size_t shm = sizeof(uint16_t) * 16 * RT * (size_t)((N + 15) / 16);
+    hipLaunchKernelGGL((route_moments_kernel<D, RT>), dim3(H * gph), dim3(256), shm, s, qbar, kbar,
+                       static_cast<const float*>(mom), N, gph, c, beta, static_cast<const float*>(nullptr), tau,
+                       static_cast<int32_t*>(nullptr), static_cast<uint32_t*>(nullptr), (N + 31) / 32, queues,
+                       tau_cmp, 0);
     return hipGetLastError();
 }
 
@@ -707,6 +738,13 @@ hipError_t launch_pooled_to_bf16(const float* kbar, const float* vsum, size_t n,
 hipError_t launch_reset_counters(int* queues, hipStream_t s) {
     hipLaunchKernelGGL(reset_counters_kernel, dim3(1), dim3(64), 0, s, queues);
     return hipGetLastError();
+}
+
+hipError_t launch_thresholds(const float* qbar, const float* kbar, int H, int N, int d, float c, float beta,
+                             float* tau, float* tau_cmp, float* mom, int* queues, hipStream_t s) {
+    if (d == 64) return thresholds_t<64>(qbar, kbar, mom, H, N, c, beta, tau, tau_cmp, queues, s);
+    if (d == 128) return thresholds_t<128>(qbar, kbar, mom, H, N, c, beta, tau, tau_cmp, queues, s);
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_route(const float* qbar, const float* kbar, int H, int N, int d, float c,

@@ -155,7 +155,7 @@ __global__ void __launch_bounds__(64) group_pick_kernel(const unsigned long long
     if (lane == 0) stride[h] = bs;
 }
 
-template <int D, int BLK, bool DENSE>
+template <int D, int BLK, bool DENSE, bool ROUTE = false>
 __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
     using S = Sweep<D, BLK>;
     // two tile buffers as four distinct objects, so the compiler can tell
@@ -248,7 +248,7 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
         }
         const int h = item / NG, gi = item % NG;
         // the head's group stride (group_pick_kernel)
-        const int st = (!DENSE && S::QB > 1 && a.gcost) ? a.gstride[h] : 1;
+        const int st = (!DENSE && !ROUTE && S::QB > 1 && a.gcost) ? a.gstride[h] : 1;
         const GroupMap gm = group_map<S::QB>(gi, N, st);
         const int nqb = gm.nqb;  // valid query blocks in this group
         // first row of this wave's 32 (rows of query block myb of the group)
@@ -260,11 +260,90 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             T = N;
         } else {
             // ---- 1. the tile list ------------------------------------------
-            // selection bits of the group's query blocks (written by the
-            // routing kernel: bit j of block i is s_ij > tau_i)
-            for (int t = tid; t < S::QB * nwords; t += S::NT) {
-                const int b = t / nwords, w = t % nwords;
-                selbits[t] = b < nqb ? a.sel[((size_t)h * N + gm.blk0 + b * gm.bstep) * a.W + w] : 0u;
+            // selection bits of the group's query blocks: bit j of block i
+            // is s_ij > tau_i
+            if constexpr (ROUTE) {
+                // routed here ("Sol-Attn" visual explainer, Eq. (4) and
+                // Eq. (11)): the proxy score of block i and key block j is
+                // qbar_i . kbar_j / sqrt(d), the column mean over block i's
+                // query tokens of their scores against pooled key j.  It is
+                // formed in fp32 from the fp32 pooled vectors (the bf16 MFMA
+                // operands of the approximate tiles would move decisions by
+                // more than the rounding of an fp32 score) and compared with
+                // the block's threshold as each word of 32 key blocks
+                // appears; the words live in LDS for this group only.
+                float* qs = reinterpret_cast<float*>(K0);  // [QB][D] pooled queries; K0 holds no tile yet
+                for (int x = tid; x < S::QB * D; x += S::NT) {
+                    const int b = x / D, e = x % D;
+                    qs[x] = b < nqb ? a.qbar[((size_t)h * N + gm.blk0 + b * gm.bstep) * D + e] : 0.0f;
+                }
+                __syncthreads();
+                constexpr int DQ = D / 4;                 // a key row is split over 4 lanes
+                const int qd = lane & 3, kl = lane >> 2;  // quarter of d, key of 16
+                float tc[S::QB];
+#pragma unroll
+                for (int b = 0; b < S::QB; ++b)
+                    tc[b] = b < nqb ? a.tau_cmp[(size_t)h * N + gm.blk0 + b * gm.bstep] : INFINITY;
+                const float* kh = a.kbar + (size_t)h * N * D;
+                for (int wd = wave; wd < nwords; wd += 4) {
+                    uint32_t word[S::QB];
+#pragma unroll
+                    for (int b = 0; b < S::QB; ++b) word[b] = 0u;
+#pragma unroll 1
+                    for (int half = 0; half < 2; ++half) {
+                        const int j = 32 * wd + 16 * half + kl;
+                        const float4* kr = reinterpret_cast<const float4*>(kh + (size_t)min(j, N - 1) * D + qd * DQ);
+                        float acc[S::QB];
+#pragma unroll
+                        for (int b = 0; b < S::QB; ++b) acc[b] = 0.0f;
+#pragma unroll
+                        for (int e4 = 0; e4 < DQ / 4; ++e4) {
+                            const float4 kv = kr[e4];
+#pragma unroll
+                            for (int b = 0; b < S::QB; ++b) {
+                                const float4 qv = *reinterpret_cast<const float4*>(qs + b * D + qd * DQ + 4 * e4);
+                                acc[b] = __builtin_fmaf(qv.x, kv.x, acc[b]);
+                                acc[b] = __builtin_fmaf(qv.y, kv.y, acc[b]);
+                                acc[b] = __builtin_fmaf(qv.z, kv.z, acc[b]);
+                                acc[b] = __builtin_fmaf(qv.w, kv.w, acc[b]);
+                            }
+                        }
+#pragma unroll
+                        for (int b = 0; b < S::QB; ++b) {
+                            acc[b] += __shfl_xor(acc[b], 1);
+                            acc[b] += __shfl_xor(acc[b], 2);
+                            // bit 4k of m: key 16 half + k of the word
+                            const uint64_t m = __ballot(qd == 0 && j < N && acc[b] * a.c > tc[b]);
+                            uint32_t v16 = 0;
+#pragma unroll
+                            for (int k2 = 0; k2 < 16; ++k2) v16 |= (uint32_t)((m >> (4 * k2)) & 1u) << k2;
+                            word[b] |= v16 << (16 * half);
+                        }
+                    }
+                    if (lane == 0)
+#pragma unroll
+                        for (int b = 0; b < S::QB; ++b) selbits[b * nwords + wd] = word[b];
+                }
+                __syncthreads();
+                // kept counts, and the decision bits when asked for
+                for (int b = wave; b < nqb; b += 4) {
+                    int cnt = 0;
+                    for (int w = lane; w < nwords; w += 64) cnt += __popc(selbits[b * nwords + w]);
+#pragma unroll
+                    for (int off = 32; off >= 1; off >>= 1) cnt += __shfl_xor(cnt, off);
+                    if (lane == 0) a.kept_out[(size_t)h * N + gm.blk0 + b * gm.bstep] = cnt;
+                }
+                if (a.sel_out)
+                    for (int t = tid; t < nqb * nwords; t += S::NT) {
+                        const int b = t / nwords, w = t % nwords;
+                        a.sel_out[((size_t)h * N + gm.blk0 + b * gm.bstep) * a.W + w] = selbits[t];
+                    }
+            } else {
+                // written by the routing kernel
+                for (int t = tid; t < S::QB * nwords; t += S::NT) {
+                    const int b = t / nwords, w = t % nwords;
+                    selbits[t] = b < nqb ? a.sel[((size_t)h * N + gm.blk0 + b * gm.bstep) * a.W + w] : 0u;
+                }
             }
             __syncthreads();
             if (wave == 0) {
@@ -708,10 +787,10 @@ int device_cus() {
     return cus;
 }
 
-template <int D, int BLK, bool DENSE>
+template <int D, int BLK, bool DENSE, bool ROUTE = false>
 hipError_t sweep_t(const AttnArgs& a, hipStream_t s) {
     using S = Sweep<D, BLK>;
-    auto kern = sweep_bf16_kernel<D, BLK, DENSE>;
+    auto kern = sweep_bf16_kernel<D, BLK, DENSE, ROUTE>;
     const int NC = (a.N + S::TB - 1) / S::TB;
     // selection bits of the group's query blocks, then at most NC approximate
     // and ceil(N / KPT) exact tile-list entries (at B = 32 up to 8 more: one
@@ -729,7 +808,7 @@ hipError_t sweep_t(const AttnArgs& a, hipStream_t s) {
             per_cu = 1;
         grid = device_cus() * per_cu;
     }
-    if (!DENSE && S::QB > 1 && a.gcost) {
+    if (!DENSE && !ROUTE && S::QB > 1 && a.gcost) {
         const int P = group_cost_parts(a.N, BLK);
         hipLaunchKernelGGL((group_cost_kernel<S::QB>), dim3(a.H * kMaxStride * P), dim3(256), 0, s, a.sel, a.N,
                            a.W, P, a.gcost);
@@ -744,6 +823,16 @@ hipError_t sweep_t(const AttnArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_sweep_bf16(const AttnArgs& a, int d, int B, bool dense, hipStream_t s) {
+    if (a.tau_cmp && !dense) {  // routing inside the sweep
+        if (!a.kept_out) return hipErrorInvalidValue;
+        if (d == 64 && B == 32) return sweep_t<64, 32, false, true>(a, s);
+        if (d == 128 && B == 32) return sweep_t<128, 32, false, true>(a, s);
+        if (d == 64 && B == 64) return sweep_t<64, 64, false, true>(a, s);
+        if (d == 64 && B == 128) return sweep_t<64, 128, false, true>(a, s);
+        if (d == 128 && B == 64) return sweep_t<128, 64, false, true>(a, s);
+        if (d == 128 && B == 128) return sweep_t<128, 128, false, true>(a, s);
+        return hipErrorInvalidValue;
+    }
     // (the dense kernel runs with B = 64 only)
     if (d == 64 && B == 32 && !dense) return sweep_t<64, 32, false>(a, s);
     if (d == 128 && B == 32 && !dense) return sweep_t<128, 32, false>(a, s);

@@ -215,12 +215,27 @@ int sol_attn_fwd_dbg(const void* q, const void* k, const void* v,
  *                    scores, ties to the lower block index, instead of
  *                    s_ij > tau_i; beta is ignored, tau receives the k-th
  *                    largest score (+inf for k = 0) and kept_counts = k.
+ *   SOL_FUSED_ROUTE  the routing as the pages' fused kernel does it ("Sol-Attn"
+ *                    visual explainer, "How the fused kernel executes it",
+ *                    Eq. (11); Eq. (5)): the thresholds come first, from the
+ *                    Eq. (5) key moments (mean pooled key and covariance about
+ *                    it, fp64) for every N, and no decision is computed or
+ *                    stored before the sweep; each workgroup forms its query
+ *                    blocks' proxy scores qbar_i . kbar_j / sqrt(d) in fp32, 32
+ *                    key blocks at a time, compares them with tau_i, builds its
+ *                    tile list from those decisions and writes its kept
+ *                    counts.  No decision map exists in device memory unless
+ *                    sel_mask asks for it.  Decisions agree with the default
+ *                    route except within fp32 rounding of tau_i; query blocks
+ *                    are grouped consecutively.  Not with SOL_TOPK.
  * flags = 0 is sol_attn_fwd_dbg.  Other arguments as sol_attn_fwd_dbg.
- * Errors: unknown flag bits, or SOL_TOPK with keep_frac outside [0, 1] or
- * NaN: SOL_EINVAL; nonzero flags with SOL_F32: SOL_EUNSUPPORTED.
+ * Errors: unknown flag bits, SOL_TOPK with SOL_FUSED_ROUTE, or SOL_TOPK with
+ * keep_frac outside [0, 1] or NaN: SOL_EINVAL; nonzero flags with SOL_F32:
+ * SOL_EUNSUPPORTED.
  */
 #define SOL_DROP_APPROX 1u
 #define SOL_TOPK 2u
+#define SOL_FUSED_ROUTE 4u
 int sol_attn_fwd_variant(const void* q, const void* k, const void* v,
                          int H, int L, int d, int B, float beta, float keep_frac,
                          unsigned flags, sol_dtype_t dt, void* out, int32_t* kept_counts,

@@ -158,7 +158,7 @@ def test_variant_rejects_bad_flags_and_fractions(lib):
     # (q, k, v, H, L, d, B, beta, keep_frac, flags, dt, out, kept, ws, ws_bytes, stream, mask, tau)
     ok = [FAKE, FAKE, FAKE, 1, 100, 64, 64, 1.0, 0.5, 0, 0, FAKE, FAKE, FAKE_WS, 1 << 30, None,
           None, None]
-    for i, val, want in [(9, 4, -1), (9, 2 | 8, -1), (8, math.nan, -1), (8, -0.1, -1),
+    for i, val, want in [(9, 8, -1), (9, 2 | 8, -1), (9, 2 | 4, -1), (8, math.nan, -1), (8, -0.1, -1),
                          (8, 1.5, -1), (10, 1, -2)]:
         bad = list(ok)
         bad[i] = val
