@@ -520,7 +520,7 @@ def main():
         "exact_tile_mfma_util": head["F_exact"] / (st["sweep"] * 1e-3) / 1e12 / peak,
         "roofline": {"bound": "mfma" if w.dtype == "bf16" else "alu", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": traffic, "kernel": (f"sweep_bf16_kernel<{d}, {B}, false>" if w.dtype == "bf16"
+                     "traffic": traffic, "kernel": (f"sweep_bf16_kernel<{d}, {B}, false, false>" if w.dtype == "bf16"
                                                     else f"attn_f32_kernel<{d}, {B}, false>"),
                      "algorithmic_flop_per_launch": F_alg},
         "stage_ms": st,
