@@ -257,7 +257,8 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
     // wave w takes 16-key tiles w, w + 4, ...  Lane (l16, g) feeds the MFMA
     // its row's (A) and its key's (B) entries d = g D/4 + s at step s, the
     // same order of d on both sides, so the 32 steps contract all of d.  The
-    // next key tile's entries load while the current one is multiplied.
+    // entries of a wave's next two key tiles load while the current one is
+    // multiplied.
     const int l16 = lane & 15, g = lane >> 4;
     constexpr int QD = D / 4;
     float qv[QD];
@@ -289,15 +290,19 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
         for (int x = 0; x < 4; ++x)
             if (4 * g + x < R && j < N) rows[(4 * g + x) * N + j] = acc[x] * c;
     };
-    float kva[QD], kvb[QD];
+    float kva[QD], kvb[QD], kvc[QD];
     if (wave < NKT) kload(wave, kva);
+    if (wave + 4 < NKT) kload(wave + 4, kvb);
 #pragma unroll 1
-    for (int kt = wave; kt < NKT; kt += 8) {
-        if (kt + 4 < NKT) kload(kt + 4, kvb);
+    for (int kt = wave; kt < NKT; kt += 12) {
+        if (kt + 8 < NKT) kload(kt + 8, kvc);
         score(kt, kva);
         if (kt + 4 >= NKT) break;
-        if (kt + 8 < NKT) kload(kt + 8, kva);
+        if (kt + 12 < NKT) kload(kt + 12, kva);
         score(kt + 4, kvb);
+        if (kt + 8 >= NKT) break;
+        if (kt + 16 < NKT) kload(kt + 16, kvb);
+        score(kt + 8, kvc);
     }
     __syncthreads();
 
@@ -585,15 +590,19 @@ __global__ void __launch_bounds__(256) route_moments_kernel(
                 if (l16 == 0) bits16[(16 * rt + 4 * g + x) * NKT + kt] = static_cast<uint16_t>(m >> (16 * g));
             }
     };
-    float kva[QD], kvb[QD];
+    float kva[QD], kvb[QD], kvc[QD];
     if (wave < NKT) kload(wave, kva);
+    if (wave + 4 < NKT) kload(wave + 4, kvb);
 #pragma unroll 1
-    for (int kt = wave; kt < NKT; kt += 8) {
-        if (kt + 4 < NKT) kload(kt + 4, kvb);
+    for (int kt = wave; kt < NKT; kt += 12) {
+        if (kt + 8 < NKT) kload(kt + 8, kvc);
         decide(kt, kva);
         if (kt + 4 >= NKT) break;
-        if (kt + 8 < NKT) kload(kt + 8, kva);
+        if (kt + 12 < NKT) kload(kt + 12, kva);
         decide(kt + 4, kvb);
+        if (kt + 8 >= NKT) break;
+        if (kt + 16 < NKT) kload(kt + 16, kvb);
+        decide(kt + 8, kvc);
     }
     __syncthreads();
 
