@@ -392,8 +392,10 @@ template <int D>
 __global__ void __launch_bounds__(256) key_moments_kernel(const float* __restrict__ kbar, int N,
                                                           float* __restrict__ mom) {
     constexpr int NBK = D / 32;
-    __shared__ float ka[64][33];    // centred keys (centred in fp64, rounded once)
-    __shared__ float kb[64][33];
+    constexpr int CR = 128;         // key rows per chunk
+    constexpr int PT = CR * 32 / 256;  // entries of each operand per thread and chunk
+    __shared__ float ka[CR][33];    // centred keys (centred in fp64, rounded once)
+    __shared__ float kb[CR][33];
     __shared__ double part[4][64];  // partial column sums
     __shared__ double mean[64];     // mbar at columns 32 bi + e (e < 32), 32 bj + e - 32
     const int h = blockIdx.x / (NBK * NBK);
@@ -402,12 +404,21 @@ __global__ void __launch_bounds__(256) key_moments_kernel(const float* __restric
     const float* kh = kbar + (size_t)h * N * D;
     auto col_of = [&](int e) { return e < 32 ? 32 * bi + e : 32 * bj + e - 32; };
 
-    // pass 1: mbar.  Thread (p, e) sums rows j = p, p + 4, ... of column e.
+    // pass 1: mbar.  Thread (p, e) sums rows j = p, p + 4, ... of column e,
+    // in that order (eight loads in flight at a time).
     {
         const int e = tid & 63, p = tid >> 6;
         const int col = col_of(e);
         double s = 0.0;
-        for (int j = p; j < N; j += 4) s += static_cast<double>(kh[(size_t)j * D + col]);
+        int j = p;
+        for (; j + 28 < N; j += 32) {
+            float x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = kh[(size_t)(j + 4 * u) * D + col];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += static_cast<double>(x[u]);
+        }
+        for (; j < N; j += 4) s += static_cast<double>(kh[(size_t)j * D + col]);
         part[p][e] = s;
     }
     __syncthreads();
@@ -418,19 +429,34 @@ __global__ void __launch_bounds__(256) key_moments_kernel(const float* __restric
     // 16 x 16 quarter (rows 16 (w >> 1), columns 16 (w & 1) of the block) with
     // fp64 matrix instructions, four key rows per instruction: A[i][k] is
     // column 16 (w >> 1) + i of row k, B[k][j] column 16 (w & 1) + j of row k.
+    // The next chunk's rows load into registers while the current one is
+    // multiplied.
     const int wave = tid >> 6, lane = tid & 63;
     const int ti = wave >> 1, tj = wave & 1;
     f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
-    for (int j0 = 0; j0 < N; j0 += 64) {
-        __syncthreads();
-        for (int x = tid; x < 64 * 32; x += 256) {
-            const int jj = x >> 5, e = x & 31, j = j0 + jj;
-            ka[jj][e] = j < N ? static_cast<float>(static_cast<double>(kh[(size_t)j * D + 32 * bi + e]) - mean[e]) : 0.0f;
-            kb[jj][e] = j < N ? static_cast<float>(static_cast<double>(kh[(size_t)j * D + 32 * bj + e]) - mean[32 + e]) : 0.0f;
+    float ra[PT], rb[PT];  // entry tid + 256 u of the chunk: row (tid + 256 u) / 32, column (tid + 256 u) % 32
+    auto fetch = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < PT; ++u) {
+            const int x = tid + 256 * u, j = j0 + (x >> 5), e = x & 31;
+            ra[u] = j < N ? kh[(size_t)j * D + 32 * bi + e] : 0.0f;
+            rb[u] = j < N ? kh[(size_t)j * D + 32 * bj + e] : 0.0f;
+        }
+    };
+    fetch(0);
+    for (int j0 = 0; j0 < N; j0 += CR) {
+        __syncthreads();  // the previous chunk's products are done
+#pragma unroll
+        for (int u = 0; u < PT; ++u) {
+            const int x = tid + 256 * u, jj = x >> 5, e = x & 31;
+            const bool in = j0 + jj < N;
+            ka[jj][e] = in ? static_cast<float>(static_cast<double>(ra[u]) - mean[e]) : 0.0f;
+            kb[jj][e] = in ? static_cast<float>(static_cast<double>(rb[u]) - mean[32 + e]) : 0.0f;
         }
         __syncthreads();
+        if (j0 + CR < N) fetch(j0 + CR);
 #pragma unroll
-        for (int k0 = 0; k0 < 64; k0 += 4) {
+        for (int k0 = 0; k0 < CR; k0 += 4) {
             const double av = static_cast<double>(ka[k0 + (lane >> 4)][16 * ti + (lane & 15)]);
             const double bv = static_cast<double>(kb[k0 + (lane >> 4)][16 * tj + (lane & 15)]);
             acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
