@@ -155,7 +155,7 @@ __global__ void __launch_bounds__(256) pooled_to_bf16_kernel(const float* __rest
 // route: per (head h, query block i) the proxy row s_i. over all N key
 // blocks (Eq. (11) right-hand side), its population mean and standard
 // deviation (Eq. (5)), tau_i = mu_i + beta sigma_i and the kept count
-// |{j : s_ij > tau_i}| (Eq. (4)).  One workgroup (256 threads) serves R
+// |{j : s_ij > tau_i}| (Eq. (4)).  One workgroup (8 waves) serves R
 // consecutive query blocks of one head (R <= 16: one MFMA row tile), so each
 // pooled key is read once per R rows; the rows live in dynamic LDS only.
 // The decisions leave as bits (one ballot per 64 key blocks), which both
@@ -165,7 +165,7 @@ __global__ void __launch_bounds__(256) pooled_to_bf16_kernel(const float* __rest
 // with (every query block keeps the same share of key blocks, the highest
 // proxy scores first): each of the
 // nr rows keeps its k largest scores, ties to the lower block index.  Wave
-// w ranks rows w, w + 4, ... held in LDS: the k-th largest score is found
+// w ranks rows w, w + nw, ... held in LDS: the k-th largest score is found
 // exactly by a binary search over order-preserving 32-bit keys (counts from
 // ballots), then every larger score is kept, and of the scores equal to it
 // the lowest-index ones until k are kept.  tau = that k-th largest score
@@ -198,10 +198,10 @@ __device__ __forceinline__ int count_at_least(const float* row, const uint32_t (
 
 template <bool REG>
 __device__ __forceinline__ void route_rows_topk(const float* rows, int N, int nr, int k, int wave, int lane,
-                                uint32_t* sel, int W, float* tau, int32_t* kept) {
+                                uint32_t* sel, int W, float* tau, int32_t* kept, int nw) {
     constexpr int MAXC = REG ? 32 : 1;  // keys held in registers: N <= 64 MAXC
     const int nch = (N + 63) / 64;
-    for (int r = wave; r < nr; r += 4) {
+    for (int r = wave; r < nr; r += nw) {
         const float* row = rows + r * N;
         uint32_t kr[MAXC];  // key of block 64 c + lane (0, never counted, past N)
 #pragma unroll
@@ -237,7 +237,7 @@ __device__ __forceinline__ void route_rows_topk(const float* rows, int N, int nr
 }
 
 template <int D, int R>
-__global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qbar,
+__global__ void __launch_bounds__(512) route_kernel(const float* __restrict__ qbar,
                                                     const float* __restrict__ kbar, int N,
                                                     int groups_per_head, float c, float beta,
                                                     const float* __restrict__ tau_in,
@@ -254,11 +254,12 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
 
     // Proxy rows by fp32 MFMA (v_mfma_f32_16x16x4_f32): the workgroup's
     // rows are one 16-row tile (rows past R or N are formed and not kept);
-    // wave w takes 16-key tiles w, w + 4, ...  Lane (l16, g) feeds the MFMA
+    // wave w takes 16-key tiles w, w + 8, ...  Lane (l16, g) feeds the MFMA
     // its row's (A) and its key's (B) entries d = g D/4 + s at step s, the
     // same order of d on both sides, so the 32 steps contract all of d.  The
-    // entries of a wave's next two key tiles load while the current one is
-    // multiplied.
+    // entries of a wave's next key tile load while the current one is
+    // multiplied (eight waves per workgroup, four per SIMD with two
+    // workgroups per CU, hide the rest of the latency).
     const int l16 = lane & 15, g = lane >> 4;
     constexpr int QD = D / 4;
     float qv[QD];
@@ -290,19 +291,16 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
         for (int x = 0; x < 4; ++x)
             if (4 * g + x < R && j < N) rows[(4 * g + x) * N + j] = acc[x] * c;
     };
-    float kva[QD], kvb[QD], kvc[QD];
+    constexpr int NW = 8;
+    float kva[QD], kvb[QD];
     if (wave < NKT) kload(wave, kva);
-    if (wave + 4 < NKT) kload(wave + 4, kvb);
 #pragma unroll 1
-    for (int kt = wave; kt < NKT; kt += 12) {
-        if (kt + 8 < NKT) kload(kt + 8, kvc);
+    for (int kt = wave; kt < NKT; kt += 2 * NW) {
+        if (kt + NW < NKT) kload(kt + NW, kvb);
         score(kt, kva);
-        if (kt + 4 >= NKT) break;
-        if (kt + 12 < NKT) kload(kt + 12, kva);
-        score(kt + 4, kvb);
-        if (kt + 8 >= NKT) break;
-        if (kt + 16 < NKT) kload(kt + 16, kvb);
-        score(kt + 8, kvc);
+        if (kt + NW >= NKT) break;
+        if (kt + 2 * NW < NKT) kload(kt + 2 * NW, kva);
+        score(kt + NW, kvb);
     }
     __syncthreads();
 
@@ -310,15 +308,15 @@ __global__ void __launch_bounds__(256) route_kernel(const float* __restrict__ qb
         uint32_t* srows = sel ? sel + ((size_t)h * N + i0) * W : nullptr;
         if (N <= 64 * 32)
             route_rows_topk<true>(rows, N, nr, topk, wave, lane, srows, W, tau_out + (size_t)h * N + i0,
-                                  kept + (size_t)h * N + i0);
+                                  kept + (size_t)h * N + i0, NW);
         else
             route_rows_topk<false>(rows, N, nr, topk, wave, lane, srows, W, tau_out + (size_t)h * N + i0,
-                                   kept + (size_t)h * N + i0);
+                                   kept + (size_t)h * N + i0, NW);
         return;
     }
-    // statistics: wave w handles rows w, w+4, ... (lane-strided sums in a
+    // statistics: wave w handles rows w, w+8, ... (lane-strided sums in a
     // fixed order, then a butterfly whose result every lane shares)
-    for (int r = wave; r < nr; r += 4) {
+    for (int r = wave; r < nr; r += NW) {
         const float* row = rows + r * N;
         float part = 0.0f, lo = INFINITY, hi = -INFINITY;
         for (int j = lane; j < N; j += 64) {
@@ -678,7 +676,7 @@ hipError_t route_t(const float* qbar, const float* kbar, int H, int N, float c, 
                    int topk, hipStream_t s) {
     const int gph = (N + R - 1) / R;
     const size_t shm = sizeof(float) * (size_t)R * N;
-    hipLaunchKernelGGL((route_kernel<D, R>), dim3(H * gph), dim3(256), shm, s, qbar, kbar, N, gph, c,
+    hipLaunchKernelGGL((route_kernel<D, R>), dim3(H * gph), dim3(512), shm, s, qbar, kbar, N, gph, c,
                        beta, tau_in, tau, kept, sel, (N + 31) / 32, queues, topk);
     return hipGetLastError();
 }
