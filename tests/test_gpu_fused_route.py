@@ -126,7 +126,8 @@ def test_fused_route_equal_keys_select_nothing(B):
     assert s["flips"] == 0 and s["kept_frac"] == 0.0
 
 
-@pytest.mark.parametrize("wl,beta,heads", [("C3", 1.0, [0, 21, 39]), ("C6b", 1.25, [0, 23])])
+@pytest.mark.parametrize("wl,beta,heads", [("C3", 1.0, [0, 21, 39]), ("C6b", 1.25, [0, 23]),
+                                            ("C4", 1.0, [0, 23]), ("C5", 1.0, [0, 23])])
 def test_fused_route_full_size(wl, beta, heads):
     w = gen.WORKLOADS[wl]
     inp = gen.generate(w, heads=heads)
