@@ -62,7 +62,8 @@ struct Sweep : TileLayout<D> {
     // tile-list entry: bit 31 approximate; bits PS .. 30 the query blocks
     // that use it; bits 0 .. PS-1 the chunk or key block index.  Exact
     // entries at B = 32 instead hold two key blocks: j1 in bits 0 .. 12, j2
-    // in bits 13 .. 25, bit 26 set when j2 is present.
+    // in bits 13 .. 25, bit 26 set when j2 is present (bits PS .. 30: the
+    // query blocks that selected both, as in every entry).
     static constexpr int PB = QB < 2 ? 2 : QB;
     static constexpr int PS = 31 - PB;
 };
@@ -412,10 +413,10 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                             const int q = p >= 0 ? 1 : 0;  // the pending block takes the first one
                             if (part == mk) {
                                 if (q && r == 0) {
-                                    tiles[nt] = (uint32_t)p | ((uint32_t)j << 13) | (1u << 26);
+                                    tiles[nt] = (uint32_t)p | ((uint32_t)j << 13) | (1u << 26) | (mk << S::PS);
                                 } else if (((r - q) & 1) == 0 && r + 1 < c) {
                                     // j1 of a pair whose j2 is the next block of mask mk
-                                    tiles[nt + q + ((r - q) >> 1)] = (uint32_t)j;
+                                    tiles[nt + q + ((r - q) >> 1)] = (uint32_t)j | (mk << S::PS);
                                 }
                             }
                             if (part == mk && r >= q && ((r - q) & 1) == 1)
@@ -431,7 +432,7 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                     // blocks still waiting: a tile each (no second half)
                     const uint64_t wb = __ballot(lane >= 1 && lane <= (int)all_blocks && pend >= 0);
                     if (lane >= 1 && lane <= (int)all_blocks && pend >= 0)
-                        tiles[nt + __popcll(wb & ((1ull << lane) - 1ull))] = (uint32_t)pend;
+                        tiles[nt + __popcll(wb & ((1ull << lane) - 1ull))] = (uint32_t)pend | ((uint32_t)lane << S::PS);
                     nt += __popcll(wb);
                 }
                 if (lane == 0) misc_s[1] = nt;
@@ -526,19 +527,19 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             decode(w_t, t, approx, part, row0);
             // B = 32 pairs: bit h of halves: this wave's query block selected
             // key block h of the pair; lim_h: keys of half h before L
+            // this wave's query block uses tile t (a B = 32 pair entry carries
+            // the query blocks that selected both of its key blocks)
+            const bool mine = ((part >> myb) & 1u) != 0u;
             uint32_t halves = 3u;
             int lim_h[2] = {0, 0};
             if (S::KPT == 2 && !approx) {
                 int j1, j2;
                 bool has2;
                 pair_of(w_t, j1, j2, has2);
-                const uint32_t* sb = selbits + myb * nwords;
-                halves = ((sb[j1 >> 5] >> (j1 & 31)) & 1u) | (has2 ? ((sb[j2 >> 5] >> (j2 & 31)) & 1u) << 1 : 0u);
+                halves = mine ? (has2 ? 3u : 1u) : 0u;
                 lim_h[0] = L - 32 * j1;
                 lim_h[1] = L - 32 * j2 + 32;
             }
-            // this wave's query block uses tile t
-            const bool mine = S::KPT == 2 && !approx ? halves != 0u : ((part >> myb) & 1u) != 0u;
             if (t + 1 < TS) {  // tile t+1 streams into (Kn, Vn)
                 uint32_t extra;
                 if constexpr (S::KPT == 2) {
