@@ -525,11 +525,11 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
             uint32_t part;
             int row0;
             decode(w_t, t, approx, part, row0);
-            // B = 32 pairs: bit h of halves: this wave's query block selected
-            // key block h of the pair; lim_h: keys of half h before L
             // this wave's query block uses tile t (a B = 32 pair entry carries
             // the query blocks that selected both of its key blocks)
             const bool mine = ((part >> myb) & 1u) != 0u;
+            // B = 32 pairs: bit h of halves: this wave's query block selected
+            // key block h of the pair; lim_h: keys of half h before L
             uint32_t halves = 3u;
             int lim_h[2] = {0, 0};
             if (S::KPT == 2 && !approx) {
