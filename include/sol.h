@@ -112,8 +112,9 @@ int sol_route(const float* qbar, const float* kbar, int H, int L, int d, int B,
  * qbar, kbar, vsum : DEVICE fp32 [H][N][d] as written by sol_pool.
  * tau       : DEVICE fp32 [H][N] as written by sol_route.
  * workspace : DEVICE, at least sol_workspace_bytes(H, L, d, B) bytes,
- *             256-byte aligned (scratch: work counters and bf16 copies of the
- *             pooled keys and summed values).
+ *             256-byte aligned (scratch: work counters, bf16 copies of the
+ *             pooled keys and summed values, and the query-block grouping
+ *             costs and strides; see sol_attn_fwd).
  * sel_bits  : DEVICE, the decisions sol_route wrote for these thresholds, or
  *             NULL.  When given, the sweep takes its decisions from them and
  *             launches no routing pass of its own; when NULL it first derives
