@@ -380,9 +380,10 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                 if constexpr (S::KPT == 1) {
                     for (int j0 = 0; j0 < N; j0 += 64) {
                         const int j = j0 + lane;
-                        uint32_t part = 0;
+                        uint32_t part = 0;  // rows of blocks past the group's last are zero
                         if (j < N)
-                            for (int b = 0; b < nqb; ++b)
+#pragma unroll
+                            for (int b = 0; b < S::QB; ++b)
                                 part |= ((selbits[b * nwords + (j >> 5)] >> (j & 31)) & 1u) << b;
                         const uint64_t m = __ballot(part != 0);
                         if (part) tiles[nt + __popcll(m & ((1ull << lane) - 1ull))] = (part << S::PS) | j;
@@ -392,42 +393,89 @@ __global__ void __launch_bounds__(256, 2) sweep_bf16_kernel(AttnArgs a) {
                     // B = 32: key blocks that the same query blocks select
                     // share a 64-key tile, so both halves of a tile serve the
                     // same waves.  Key blocks are taken in ascending order;
-                    // lane m of `pend` holds a block with selection mask m
-                    // still waiting for a partner (-1: none).  In a chunk of
-                    // 64 blocks, those of mask m pair up in order, the first
-                    // with the pending one; an odd last one waits.  Blocks
-                    // left waiting at the end get a tile of their own.
+                    // lane m (1 <= m <= all_blocks) keeps the state of
+                    // selection mask m: `pend`, a block of mask m still
+                    // waiting for a partner (-1: none).  In a chunk of 64
+                    // blocks, those of mask m pair up in order, the first with
+                    // the pending one; an odd last one waits.  The chunk's
+                    // entries go out mask by mask, ascending.  Blocks left
+                    // waiting at the end get a tile of their own.
                     int pend = -1;
+                    // the selection words of the chunk from j0: lane l < 2 QB
+                    // reads word j0 / 32 + (l & 1) of row l / 2 (clamped to the
+                    // last word; bits of blocks past N are cleared below)
+                    auto chunk_word = [&](int j0) {
+                        const int w = min((j0 >> 5) + (lane & 1), nwords - 1);
+                        return selbits[((lane >> 1) & (S::QB - 1)) * nwords + w];
+                    };
+                    uint32_t wnext = chunk_word(0);
                     for (int j0 = 0; j0 < N; j0 += 64) {
-                        const int j = j0 + lane;
-                        uint32_t part = 0;
-                        if (j < N)
-                            for (int b = 0; b < nqb; ++b)
-                                part |= ((selbits[b * nwords + (j >> 5)] >> (j & 31)) & 1u) << b;
-                        for (uint32_t mk = 1; mk <= all_blocks; ++mk) {
-                            const uint64_t bm = __ballot(part == mk);
-                            if (bm == 0) continue;
-                            const int c = __popcll(bm);
-                            const int r = __popcll(bm & ((1ull << lane) - 1ull));  // rank among mask mk
-                            const int p = __builtin_amdgcn_readlane(pend, (int)mk);
-                            const int q = p >= 0 ? 1 : 0;  // the pending block takes the first one
-                            if (part == mk) {
-                                if (q && r == 0) {
-                                    tiles[nt] = (uint32_t)p | ((uint32_t)j << 13) | (1u << 26) | (mk << S::PS);
-                                } else if (((r - q) & 1) == 0 && r + 1 < c) {
-                                    // j1 of a pair whose j2 is the next block of mask mk
-                                    tiles[nt + q + ((r - q) >> 1)] = (uint32_t)j | (mk << S::PS);
-                                }
-                            }
-                            if (part == mk && r >= q && ((r - q) & 1) == 1)
-                                tiles[nt + q + ((r - q) >> 1)] |= ((uint32_t)j << 13) | (1u << 26);
-                            const int rest = c - q;  // blocks after the one the pending block took
-                            nt += q + (rest >> 1);
-                            // the new pending block of mask mk: the last one when rest is odd
-                            const int last = 63 - __builtin_clzll(bm);
-                            const int np = (rest & 1) ? __builtin_amdgcn_readlane(j, last) : -1;
-                            if (lane == (int)mk) pend = np;
+                        // the lane index, opaque here so that the lane masks
+                        // below stay in this loop instead of holding registers
+                        // through the sweep
+                        int ln = lane;
+                        asm volatile("" : "+v"(ln));
+                        const bool mlane = ln >= 1 && ln <= (int)all_blocks;
+                        const uint64_t below = (1ull << ln) - 1ull;     // lanes before this one
+                        const uint64_t above = ~((2ull << ln) - 1ull);  // lanes after it
+                        const int j = j0 + ln;
+                        const uint32_t wcur = wnext;
+                        wnext = chunk_word(j0 + 64);  // next chunk's, read while this one is built
+                        // row b's bits of the chunk's 64 blocks, lane k for block j0 + k
+                        const uint64_t valid = N - j0 >= 64 ? ~0ull : (1ull << (N - j0)) - 1ull;
+                        uint64_t rowb[S::QB], nz = 0;
+#pragma unroll
+                        for (int b = 0; b < S::QB; ++b) {
+                            const uint32_t lo = __builtin_amdgcn_readlane(wcur, 2 * b);
+                            const uint32_t hi = __builtin_amdgcn_readlane(wcur, 2 * b + 1);
+                            rowb[b] = (((uint64_t)hi << 32) | lo) & valid;
+                            nz |= rowb[b];
                         }
+                        uint32_t part = 0;  // the query blocks that selected block j
+                        // lanes of mask m = lane (1 <= m <= all_blocks)
+                        uint64_t mine = nz;
+#pragma unroll
+                        for (int b = 0; b < S::QB; ++b) {
+                            part |= (uint32_t)((rowb[b] >> ln) & 1u) << b;
+                            mine &= ((ln >> b) & 1) ? rowb[b] : ~rowb[b];
+                        }
+                        if (!mlane) mine = 0;
+                        // per mask (lane m): blocks in the chunk, the pending
+                        // block's partner taken, entries emitted, next pending
+                        const int c_m = __popcll(mine);
+                        const int q_m = (c_m > 0 && pend >= 0) ? 1 : 0;
+                        const int n_m = c_m > 0 ? q_m + ((c_m - q_m) >> 1) : 0;
+                        // inclusive prefix over each row of 16 lanes (DPP row
+                        // shifts by 1, 2, 4, 8; lanes shifted in from outside
+                        // the row read 0)
+                        int incl = n_m;
+                        incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xf, 0xf, true);
+                        incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xf, 0xf, true);
+                        incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xf, 0xf, true);
+                        incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xf, 0xf, true);
+                        // from mask lane `part`: the lanes of this block's mask,
+                        // the mask's first entry in the chunk and its pending
+                        // block (lane 0 holds no mask: zeros for part = 0)
+                        const uint64_t own = ((uint64_t)(uint32_t)__shfl((int)(uint32_t)(mine >> 32), (int)part) << 32) |
+                                             (uint32_t)__shfl((int)(uint32_t)mine, (int)part);
+                        const int fp = __shfl(((incl - n_m) << 16) | (pend & 0xffff), (int)part);
+                        const int off = fp >> 16;
+                        const int p = (int16_t)(fp & 0xffff);
+                        if (part) {
+                            const int q = p >= 0 ? 1 : 0;
+                            const int r = __popcll(own & below);  // rank among the blocks of its mask
+                            const uint32_t tag = part << S::PS;
+                            if (q && r == 0) {
+                                tiles[nt + off] = (uint32_t)p | ((uint32_t)j << 13) | (1u << 26) | tag;
+                            } else if (((r - q) & 1) == 0 && (own & above) != 0) {
+                                // j1 of a pair: j2 is the next block of the same mask
+                                const int j2 = j0 + __builtin_ctzll(own & above);
+                                tiles[nt + off + q + ((r - q) >> 1)] =
+                                    (uint32_t)j | ((uint32_t)j2 << 13) | (1u << 26) | tag;
+                            }
+                        }
+                        nt += __builtin_amdgcn_readlane(incl, 15);
+                        if (c_m > 0) pend = ((c_m - q_m) & 1) ? j0 + 63 - __builtin_clzll(mine) : -1;
                     }
                     // blocks still waiting: a tile each (no second half)
                     const uint64_t wb = __ballot(lane >= 1 && lane <= (int)all_blocks && pend >= 0);
