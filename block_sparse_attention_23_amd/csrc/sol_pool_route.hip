@@ -471,12 +471,31 @@ __global__ void __launch_bounds__(256) key_moments_kernel(const float* __restric
     if (bj == 0 && tid < 32) mh[32 * bi + tid] = static_cast<float>(mean[tid]);
 }
 
+// Three-way bf16 split of eight fp32 values: x[e] = p0 + p1 + p2 up to about
+// 2^-24 |x[e]|, where p0 is the nearest bf16 to x[e], p1 the nearest to the
+// (exact) remainder x[e] - p0 and p2 the nearest to x[e] - p0 - p1.  Value e
+// lands in element e of the bf16x8 view (element 2i in the low half of word i).
+__device__ __forceinline__ void split3_bf16x8(const float* x, u32x4_t& p0, u32x4_t& p1, u32x4_t& p2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a = x[2 * i], b = x[2 * i + 1];
+        const uint32_t u0 = pack_bf16x2(a, b);
+        const float ra = a - __uint_as_float(u0 << 16), rb = b - __uint_as_float(u0 & 0xFFFF0000u);
+        const uint32_t u1 = pack_bf16x2(ra, rb);
+        const float sa = ra - __uint_as_float(u1 << 16), sb = rb - __uint_as_float(u1 & 0xFFFF0000u);
+        p0[i] = u0;
+        p1[i] = u1;
+        p2[i] = pack_bf16x2(sa, sb);
+    }
+}
+
 // ============================================================================
 // route from the key moments, for rows too long to hold in LDS (N > 1280):
 // per (h, i) the threshold tau_i = mu_i + beta sigma_i (Eq. (4)) with mu_i
 // and sigma_i from the moments (Eq. (5), above), then one pass that forms
-// every s_ij (Eq. (11) right-hand side) exactly as the row-holding route
-// does and keeps only the decision s_ij > tau_i, as bits, and their count.
+// every s_ij (Eq. (11) right-hand side) to fp32 accuracy from bf16 splits of
+// the pooled vectors (below) and keeps only the decision s_ij > tau_i, as
+// bits, and their count.
 // One workgroup serves 16 RT query blocks (RT MFMA row tiles, each pooled-key
 // tile loaded once for all of them).  With tau_in,
 // or beta = +-inf, the thresholds need no moments.
@@ -572,15 +591,28 @@ __global__ void __launch_bounds__(256) route_moments_kernel(
         return;
     }
 
-    // decisions: the proxy scores as the row-holding route forms them (fp32
-    // MFMA, the same operands and order), compared as they leave the MFMA
+    // decisions: s_ij = c qbar_i . kbar_j from three-way bf16 splits of both
+    // vectors (x = x0 + x1 + x2, each part the nearest bf16 to what the
+    // earlier ones leave, so the rest is ~2^-24 |x|) on bf16 MFMAs: the six
+    // cross products whose part indices sum to at most 2, accumulated in
+    // fp32, give the fp32 product to about the rounding of an fp32 MFMA at
+    // 2.7x its rate.  Lane (l16, g) holds entries g D/4 .. g D/4 + D/4 - 1
+    // of its row (A) and of its key (B); step st contracts eight of them,
+    // the same d on both sides.  Each score is compared as it leaves the
+    // MFMA.
     const int l16 = lane & 15, g = lane >> 4;
     constexpr int QD = D / 4;
-    float qv[RT][QD];
+    constexpr int NST = QD / 8;  // 32-deep MFMA steps
+    u32x4_t qa[RT][NST][3];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int e = 0; e < QD; ++e) qv[rt][e] = qs[16 * rt + l16][g * QD + e];
+        for (int st = 0; st < NST; ++st) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = qs[16 * rt + l16][g * QD + 8 * st + e];
+            split3_bf16x8(x, qa[rt][st][0], qa[rt][st][1], qa[rt][st][2]);
+        }
     const float* kh = kbar + (size_t)h * N * D;
     float tr[RT][4];
 #pragma unroll
@@ -600,10 +632,20 @@ __global__ void __launch_bounds__(256) route_moments_kernel(
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) acc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int st = 0; st < QD; ++st)
+        for (int st = 0; st < NST; ++st) {
+            u32x4_t kb[3];
+            split3_bf16x8(kv + 8 * st, kb[0], kb[1], kb[2]);
+            // smallest terms first: (1,1), (0,2), (2,0), (0,1), (1,0), (0,0)
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
-                acc[rt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qv[rt][st], kv[st], acc[rt], 0, 0, 0);
+            for (int rt = 0; rt < RT; ++rt) {
+                acc[rt] = mfma16(as_bf16x8(qa[rt][st][1]), as_bf16x8(kb[1]), acc[rt]);
+                acc[rt] = mfma16(as_bf16x8(qa[rt][st][0]), as_bf16x8(kb[2]), acc[rt]);
+                acc[rt] = mfma16(as_bf16x8(qa[rt][st][2]), as_bf16x8(kb[0]), acc[rt]);
+                acc[rt] = mfma16(as_bf16x8(qa[rt][st][0]), as_bf16x8(kb[1]), acc[rt]);
+                acc[rt] = mfma16(as_bf16x8(qa[rt][st][1]), as_bf16x8(kb[0]), acc[rt]);
+                acc[rt] = mfma16(as_bf16x8(qa[rt][st][0]), as_bf16x8(kb[0]), acc[rt]);
+            }
+        }
         const int j = kt * 16 + l16;  // lane holds rows 16 rt + 4g .. 16 rt + 4g+3 of key j
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)

@@ -97,8 +97,9 @@ int sol_pool(const void* q, const void* k, const void* v,
  * sigma_i is 0 (all its scores equal) keeps no block: none is strictly above
  * tau_i = mu_i.
  * The counts and bits are those the forward pass uses (the same kernels
- * form every s_ij, by fp32 matrix instructions; both sweeps take their
- * decisions from these bits).
+ * form every s_ij: fp32 matrix instructions for N <= 1280, three-way bf16
+ * splits of the fp32 vectors, at fp32 accuracy, for longer rows; both
+ * sweeps take their decisions from these bits).
  */
 int sol_route(const float* qbar, const float* kbar, int H, int L, int d, int B,
               float beta, float* tau, int32_t* kept_counts, uint32_t* sel_bits,
