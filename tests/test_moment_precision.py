@@ -111,3 +111,89 @@ def test_equal_keys_give_zero_spread_exactly(base):
     q = qbar[0].astype(F32).astype(np.float64)
     mu = ((1.0 / np.sqrt(128)) * (q @ kbar[0, 0].astype(F32).astype(np.float64))).astype(F32)
     assert np.array_equal(tau, mu)
+
+
+# The moment route forms each proxy score s_ij = c qbar_i . kbar_j from
+# three-way bf16 splits of both fp32 vectors (x = x0 + x1 + x2, each part the
+# round-to-nearest-even bf16 of what the earlier parts leave) on bf16 matrix
+# instructions: the six cross products whose part indices sum to at most 2,
+# eight entries at a time, accumulated in fp32 in the kernel's order.  The
+# emulation below follows that arithmetic (bf16 x bf16 products are exact in
+# fp32) and checks that it keeps fp32 accuracy, so the decisions it takes
+# agree with the oracle's as closely as an fp32 dot product's would.
+
+def _bf16_rne(x):
+    u = x.astype(F32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(F32)
+
+
+def _split3(x):
+    x = x.astype(F32)
+    p0 = _bf16_rne(x)
+    r = (x - p0).astype(F32)
+    p1 = _bf16_rne(r)
+    p2 = _bf16_rne((r - p1).astype(F32))
+    return p0, p1, p2
+
+
+_SPLIT_TERMS = [(1, 1), (0, 2), (2, 0), (0, 1), (1, 0), (0, 0)]  # the kernel's order per step
+
+
+def _split_dot(q, k):
+    """The kernel's score arithmetic for one (row, key) pair, d ascending in
+    steps of eight (the order within a lane's share of d; the four lane
+    groups' shares are summed by the matrix instruction the same way)."""
+    qs, ks = _split3(q), _split3(k)
+    acc = F32(0)
+    for st in range(0, len(q), 8):
+        sl = slice(st, st + 8)
+        for i, j in _SPLIT_TERMS:
+            for p in (qs[i][sl].astype(np.float64) * ks[j][sl]).astype(F32):
+                acc = F32(acc + p)
+    return float(acc)
+
+
+def test_split_parts_represent_fp32_exactly():
+    x = (np.random.default_rng(11).standard_normal(200_000) * 10.0 ** np.random.default_rng(12).uniform(-4, 4, 200_000)).astype(F32)
+    p0, p1, p2 = _split3(x)
+    assert np.array_equal(p0.astype(np.float64) + p1 + p2, x.astype(np.float64))
+
+
+@pytest.mark.parametrize("offset", [0.0, 60.0])
+def test_split_scores_keep_fp32_accuracy(offset):
+    """Error of the split score against the fp64 dot product, relative to
+    sum |q_e k_e|: within a few times that of a sequential fp32 dot product
+    (and far inside the 1e-3 flip band), also for keys that share a large
+    common component."""
+    rng = np.random.default_rng(13)
+    worst_split = worst_f32 = 0.0
+    for _ in range(300):
+        q = (2.0 * rng.standard_normal(128)).astype(F32)
+        k = (rng.standard_normal(128) + offset).astype(F32)
+        exact = float(np.dot(q.astype(np.float64), k.astype(np.float64)))
+        scale = float(np.abs(q.astype(np.float64) * k).sum())
+        f32 = F32(0)
+        for e in range(128):
+            f32 = F32(f32 + F32(q[e] * k[e]))
+        worst_split = max(worst_split, abs(_split_dot(q, k) - exact) / scale)
+        worst_f32 = max(worst_f32, abs(float(f32) - exact) / scale)
+    assert worst_split < 1e-6
+    assert worst_split < 8 * max(worst_f32, 2.0 ** -24)
+
+
+def test_three_term_split_would_not_keep_fp32_accuracy():
+    """The cheaper three-product split (x0 y0 + x0 y1 + x1 y0) drops terms of
+    about 2^-16 relative: measurably worse than fp32, which is why the kernel
+    takes six."""
+    rng = np.random.default_rng(14)
+    worst = 0.0
+    for _ in range(200):
+        q = (2.0 * rng.standard_normal(128)).astype(F32)
+        k = rng.standard_normal(128).astype(F32)
+        qs, ks = _split3(q), _split3(k)
+        approx = sum(float(np.dot(qs[i].astype(np.float64), ks[j].astype(np.float64)))
+                     for i, j in [(0, 0), (0, 1), (1, 0)])
+        exact = float(np.dot(q.astype(np.float64), k.astype(np.float64)))
+        worst = max(worst, abs(approx - exact) / float(np.abs(q.astype(np.float64) * k).sum()))
+    assert worst > 1e-6
