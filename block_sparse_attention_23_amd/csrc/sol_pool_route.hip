@@ -403,18 +403,19 @@ __global__ void __launch_bounds__(256) key_moments_kernel(const float* __restric
     auto col_of = [&](int e) { return e < 32 ? 32 * bi + e : 32 * bj + e - 32; };
 
     // pass 1: mbar.  Thread (p, e) sums rows j = p, p + 4, ... of column e,
-    // in that order (eight loads in flight at a time).
+    // in that order (32 loads in flight at a time: the pass is a chain of
+    // L2 round trips).
     {
         const int e = tid & 63, p = tid >> 6;
         const int col = col_of(e);
         double s = 0.0;
         int j = p;
-        for (; j + 28 < N; j += 32) {
-            float x[8];
+        for (; j + 124 < N; j += 128) {
+            float x[32];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) x[u] = kh[(size_t)(j + 4 * u) * D + col];
+            for (int u = 0; u < 32; ++u) x[u] = kh[(size_t)(j + 4 * u) * D + col];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) s += static_cast<double>(x[u]);
+            for (int u = 0; u < 32; ++u) s += static_cast<double>(x[u]);
         }
         for (; j < N; j += 4) s += static_cast<double>(kh[(size_t)j * D + col]);
         part[p][e] = s;
@@ -426,12 +427,14 @@ __global__ void __launch_bounds__(256) key_moments_kernel(const float* __restric
     // pass 2: Cov block (bi, bj) from the centred keys.  Wave w forms the
     // 16 x 16 quarter (rows 16 (w >> 1), columns 16 (w & 1) of the block) with
     // fp64 matrix instructions, four key rows per instruction: A[i][k] is
-    // column 16 (w >> 1) + i of row k, B[k][j] column 16 (w & 1) + j of row k.
+    // column 16 (w >> 1) + i of row k, B[k][j] column 16 (w & 1) + j of row k;
+    // rows 8 m .. 8 m + 3 go to one accumulator and 8 m + 4 .. 8 m + 7 to a
+    // second (two dependent chains of half the length), added at the end.
     // The next chunk's rows load into registers while the current one is
     // multiplied.
     const int wave = tid >> 6, lane = tid & 63;
     const int ti = wave >> 1, tj = wave & 1;
-    f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+    f64x4_t acc = {0.0, 0.0, 0.0, 0.0}, acc1 = {0.0, 0.0, 0.0, 0.0};
     float ra[PT], rb[PT];  // entry tid + 256 u of the chunk: row (tid + 256 u) / 32, column (tid + 256 u) % 32
     auto fetch = [&](int j0) __attribute__((always_inline)) {
 #pragma unroll
@@ -454,12 +457,17 @@ __global__ void __launch_bounds__(256) key_moments_kernel(const float* __restric
         __syncthreads();
         if (j0 + CR < N) fetch(j0 + CR);
 #pragma unroll
-        for (int k0 = 0; k0 < CR; k0 += 4) {
+        for (int k0 = 0; k0 < CR; k0 += 8) {
             const double av = static_cast<double>(ka[k0 + (lane >> 4)][16 * ti + (lane & 15)]);
             const double bv = static_cast<double>(kb[k0 + (lane >> 4)][16 * tj + (lane & 15)]);
             acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+            const double av1 = static_cast<double>(ka[k0 + 4 + (lane >> 4)][16 * ti + (lane & 15)]);
+            const double bv1 = static_cast<double>(kb[k0 + 4 + (lane >> 4)][16 * tj + (lane & 15)]);
+            acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(av1, bv1, acc1, 0, 0, 0);
         }
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] += acc1[r];
     const double n = static_cast<double>(N);
     float* mh = mom + (size_t)h * (D + D * D);
     // element r of lane l is row 4 r + (l >> 4) of column l & 15 (the fp64
